@@ -1,0 +1,253 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer-forward library
+ * (libmoe.so).
+ *
+ * The forward pass of one DeepSeekMoE layer, in the order the calls below
+ * run it:
+ *   router GEMM and scores  -> moe_route
+ *   group-limited top-k     -> moe_route
+ *   dispatch                -> moe_permute
+ *   SwiGLU experts          -> moe_grouped_ffn (routed experts, shared expert)
+ *   combine                 -> moe_combine
+ *   load statistics         -> moe_load_stats
+ *   all of the above        -> moe_layer_forward
+ *
+ * Sources (web pages, cited by title and section):
+ *   [EVO]   "DeepSeek MoE：从v1到v3的演进" (wln20.github.io)
+ *   [GLR]   "DeepSeek-V3的Group-Limited Expert Routing与负载均衡优化实践" (mhpn.cn)
+ *   [BUILD] "从零构建DeepSeekMoE：揭秘混合专家模型中的负载均衡与专家协同机制"
+ *   [TECH]  "DeepSeek-V3技术解密：DeepSeekMoE架构如何重塑AI模型效能边界"
+ *
+ * Conventions shared by every call:
+ *   - Every array pointer is a DEVICE pointer, allocated and owned by the
+ *     caller; the library allocates no device memory and keeps no pointer
+ *     after a call returns.  Only `cfg`, `weights` (the struct itself),
+ *     `aux` (the struct itself), `bytes` and `stage_events` are host memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise the host.  Results are ready when the
+ *     stream's work up to that point has completed.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-MOE_OK return nothing was enqueued (MOE_ERR_HIP excepted: a launch
+ *     failed part-way, and output contents are unspecified).
+ *   - Row-major layouts, element strides as stated; weights are stored
+ *     "out x in" (the reduction dimension contiguous).
+ *   - Calls that share a workspace must not overlap in time; independent
+ *     calls on different streams need their own workspaces.
+ *   - Outputs are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics on any output path).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size or inconsistent cfg */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Score function.  SIGMOID: s = 1/(1+e^-l), each expert independent
+ * ([EVO] §DeepSeek-v3).  SOFTMAX: s = softmax over the N logits ([EVO]
+ * §ST-MoE p_i(x); §DeepSeek-v1/v2 gate). */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+typedef struct {
+  int32_t T;           /* tokens in the batch (>= 0)                            */
+  int32_t H;           /* hidden size; multiple of 64                           */
+  int32_t N;           /* routed experts; 1..256, multiple of 4                 */
+  int32_t k;           /* experts chosen per token; 0..min(64, candidates)      */
+  int32_t n_groups;    /* expert groups ([GLR] §1); 1 = no group limit          */
+  int32_t topk_groups; /* groups kept per token ([GLR] §1, §3)                  */
+  int32_t group_topn;  /* keys summed into a group's score: 1 or 2              */
+  int32_t score_fn;    /* moe_score_fn                                          */
+  int32_t norm_topk;   /* 1: gates divided by the sum of the k chosen scores    */
+  float route_scale;   /* gate multiplier (1.0, or 2.5 for V3-shaped layers)    */
+  int32_t capacity;    /* per-expert capacity C; 0 = unlimited ([EVO] §GShard)  */
+  int32_t I;           /* routed expert intermediate size; multiple of 64       */
+  int32_t n_shared;    /* always-on shared experts ([EVO] §DeepSeek-v1)         */
+  int32_t I_shared;    /* intermediate size of one shared expert                */
+  int32_t act_dtype;   /* moe_dtype of x, expert activations and out            */
+  int32_t w_dtype;     /* moe_dtype of expert weights (must equal act_dtype)    */
+  int32_t router_dtype;/* moe_dtype of the router weight W_g                    */
+} moe_cfg;
+
+/* Layer weights (device pointers):
+ *   w_router [N, H]              router_dtype
+ *   w13      [N, 2*I, H]         per expert: rows [0,I) gate, rows [I,2I) up
+ *   w2       [N, H, I]           per expert: down projection
+ *   ws13     [2*n_shared*I_shared, H]  the shared experts packed as one of
+ *            width n_shared*I_shared: gate rows of every shared expert, then
+ *            their up rows, in the same expert order
+ *   ws2      [H, n_shared*I_shared]    their down columns, same order
+ * Packing the shared experts side by side is exactly their sum, since each
+ * intermediate unit of a SwiGLU expert contributes independently. */
+typedef struct {
+  const void* w_router;
+  const void* w13;
+  const void* w2;
+  const void* ws13; /* NULL iff n_shared == 0 */
+  const void* ws2;  /* NULL iff n_shared == 0 */
+} moe_weights;
+
+/* Stages of moe_layer_forward, for optional per-stage events. */
+enum {
+  MOE_STAGE_ROUTER_GEMM = 0, /* logits                                        */
+  MOE_STAGE_ROUTE = 1,       /* scores, group limit, top-k, gates, lse        */
+  MOE_STAGE_DISPATCH = 2,    /* histogram, scan, capacity, permutation        */
+  MOE_STAGE_FFN_GATE_UP = 3, /* SwiGLU first half (routed + shared)           */
+  MOE_STAGE_FFN_DOWN = 4,    /* down projection (routed + shared)             */
+  MOE_STAGE_COMBINE = 5,     /* gate-weighted combine                         */
+  MOE_STAGE_STATS = 6,       /* f, P, L_B, z                                  */
+  MOE_N_STAGES = 7
+};
+
+/* Optional outputs of moe_layer_forward; any member may be NULL (the value
+ * then lives in the workspace only).  Sizes:
+ *   logits [T,N] f32, topk_idx/topk_gate/topk_score [T,k], token_lse [T] f32,
+ *   counts [N] i32 (before capacity), offsets [N+1] i32 (after capacity),
+ *   row_token [T*k] i32 (first offsets[N] valid), inv_row [T,k] i32
+ *   (-1 = dropped), n_dropped [2] i32 = {dropped assignments, tokens with
+ *   every assignment dropped}, f [N], P [N], scalars [3] f32 = {L_B, z, z_sq}.
+ * stage_events: host array of MOE_N_STAGES+1 hipEvent_t created by the
+ * caller; event i is recorded on the stream before stage i and event
+ * MOE_N_STAGES after the last stage.  NULL = no events. */
+typedef struct {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* topk_score;
+  float* token_lse;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* inv_row;
+  int32_t* n_dropped;
+  float* f;
+  float* P;
+  float* scalars;
+  void** stage_events;
+} moe_aux;
+
+/* Bytes of workspace moe_layer_forward needs for cfg; also enough for any
+ * single granular call below with the same cfg.  Returns MOE_ERR_INVALID_ARG
+ * or MOE_ERR_UNSUPPORTED for a cfg the library rejects. */
+moe_status moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
+
+/* Router GEMM, scores, group-limited top-k and gates ([EVO] §DeepSeek-v3:
+ * sigmoid score, selection on s + b, gate from the unbiased s; [GLR] §1, §3:
+ * score groups, keep the best topk_groups, choose top-k among their experts).
+ *   x        [T,H] act_dtype, or NULL: then `logits` is an INPUT [T,N] f32
+ *            and the router GEMM is skipped
+ *   w_router [N,H] router_dtype (ignored when x == NULL)
+ *   logits   [T,N] f32: written when x != NULL (fp32-accumulated x.W_g^T,
+ *            [TECH] §四.2 keeps the router in fp32)
+ *   bias     [N] f32 or NULL: added to the score for selection only
+ *   topk_idx [T,k] i32: chosen experts, slot j = j-th largest key; ties go
+ *            to the lower expert (and group) index
+ *   topk_gate [T,k] f32: s (divided by the sum of the k chosen s when
+ *            norm_topk) times route_scale
+ *   topk_score [T,k] f32: unbiased s of the chosen expert
+ *   token_lse [T] f32: log sum_e exp(l_e), or NULL
+ * Selection keys: sigmoid -> fl32(s + b) with s from the library's fp32
+ * sigmoid (Cody-Waite reduction, degree-7 Taylor series, correctly rounded
+ * add and divide); softmax -> fl32(l + b).  Group score = fl32 sum of the
+ * group's group_topn largest keys.  Workspace: moe_workspace_size. */
+moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
+                     float* logits, const float* bias, int32_t* topk_idx,
+                     float* topk_gate, float* topk_score, float* token_lse,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch ([EVO] §GShard expert capacity; §DeepSeek-v2 drops the
+ * lowest-scored tokens first): per-expert counts, optional capacity drop,
+ * permutation.  Rows are grouped by expert (ascending), ascending token
+ * order inside an expert.  With capacity C > 0 an expert keeps its C
+ * assignments of highest topk_score (lower token first on ties).
+ *   topk_idx, topk_score [T,k]; x [T,H] act_dtype or NULL
+ *   counts [N] i32 (before capacity), offsets [N+1] i32 (after capacity),
+ *   row_token [T*k] i32, inv_row [T,k] i32 (-1 = dropped),
+ *   x_perm [T*k, H] act_dtype or NULL: x_perm[r] = x[row_token[r]] for
+ *   r < offsets[N]; n_dropped [2] i32 or NULL.
+ * Softmax scores with capacity > 0 are MOE_ERR_UNSUPPORTED. */
+moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx,
+                       const float* topk_score, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* row_token, int32_t* inv_row,
+                       void* x_perm, int32_t* n_dropped, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU experts over row segments ([EVO] §DeepSeek-v1 fine-grained
+ * experts; the expert's form is SwiGLU: y = Wd (silu(Wg a) * (Wu a))).
+ * Segment s covers rows [seg_offsets[s], seg_offsets[s+1]) and uses
+ *   w13 + s*2*inter*H ([2*inter, H]: gate rows then up rows) and
+ *   w2  + s*H*inter   ([H, inter]).
+ *   seg_offsets [n_segments+1] i32 DEVICE, non-decreasing, from 0;
+ *            NULL = one segment of max_rows rows
+ *   max_rows  upper bound on seg_offsets[n_segments] (sizes y and the
+ *            workspace); rows beyond seg_offsets[n_segments] are untouched
+ *   a        activations; row r of the problem reads a[row_index[r]] when
+ *            row_index != NULL, else a[r]; [*, H] act_dtype
+ *   y        [max_rows, H] act_dtype output
+ * act_dtype == w_dtype == bf16: bf16 MFMA, fp32 accumulate, the SwiGLU
+ * product rounded to bf16 once.  f32: fp32 arithmetic throughout.
+ * Workspace: moe_grouped_ffn_workspace_size. */
+moe_status moe_grouped_ffn(const moe_cfg* cfg, int32_t n_segments,
+                           const int32_t* seg_offsets, int32_t max_rows,
+                           int32_t inter, const void* a,
+                           const int32_t* row_index, const void* w13,
+                           const void* w2, void* y, void* ws, size_t ws_bytes,
+                           void* stream);
+moe_status moe_grouped_ffn_workspace_size(const moe_cfg* cfg, int32_t max_rows,
+                                          int32_t inter, size_t* bytes);
+
+/* Combine ([BUILD] §2.2: shared output plus routed output; [EVO] §GShard:
+ * a dropped assignment contributes nothing, the token keeps its residual
+ * outside the layer):
+ *   out[t] = y_shared[t] + sum_{j<k, inv_row[t,j] >= 0} gate[t,j] * y_perm[inv_row[t,j]]
+ * summed in fp32 in slot order, rounded once to act_dtype.
+ *   y_perm [*, H], y_shared [T,H] or NULL, out [T,H] (act_dtype). */
+moe_status moe_combine(const moe_cfg* cfg, const void* y_perm,
+                       const int32_t* inv_row, const float* topk_gate,
+                       const void* y_shared, void* out, void* stream);
+
+/* Load statistics ([EVO] §ST-MoE): f_e = counts_e / (k T);
+ * P_e = sum_t s[t,e] / sum_t sum_e' s[t,e'] (the expert's share of all
+ * score mass, all N experts, no bias); L_B = N sum_e f_e P_e;
+ * z = (1/T) sum_t LSE(l_t); z_sq = (1/T) sum_t LSE(l_t)^2.
+ *   counts [N] i32, token_lse [T] f32, logits [T,N] f32 ->
+ *   f [N] f32, P [N] f32, scalars [3] f32 = {L_B, z, z_sq}.
+ * Reductions are accumulated in fp64 in a fixed order. */
+moe_status moe_load_stats(const moe_cfg* cfg, const int32_t* counts,
+                          const float* token_lse, const float* logits, float* f,
+                          float* P, float* scalars, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Auxiliary-loss-free bias update ([EVO] §DeepSeek-v3): with c the
+ * per-expert counts and cbar their mean, b_e <- b_e + u * sign(cbar - c_e),
+ * sign(0) = 0.  bias [N] f32 updated in place. */
+moe_status moe_bias_update(const moe_cfg* cfg, const int32_t* counts,
+                           float* bias, float u, void* stream);
+
+/* The whole layer: out [T,H] = shared(x) + sum of gated routed experts.
+ * x [T,H] act_dtype; bias [N] f32 or NULL; aux NULL or as above.
+ * Workspace: moe_workspace_size(cfg). */
+moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* weights,
+                             const void* x, const float* bias, void* out,
+                             const moe_aux* aux, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Static string for a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -59,6 +59,7 @@ def lib():
         L.orc_swiglu_row.argtypes = [_i, _i, _vp, _i, _vp, _vp, _i, _vp]
         L.orc_token_output.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _vp, _vp,
                                        _vp, _vp, _vp, _i, _vp]
+        L.orc_combine.argtypes = [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]
         L.orc_load_stats.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
         L.orc_bias_update.argtypes = [_i, _vp, _vp, ctypes.c_float, _vp]
         _LIB = L
@@ -179,6 +180,22 @@ def token_output(x_row: np.ndarray, w13_sel: list, w2_sel: list, gates: np.ndarr
     out = np.empty((H,), np.float64)
     lib().orc_token_output(H, k, I, n_shared, I_sh, _ptr(x_row), _typed(x_row),
                            arr13, arr2, _ptr(g), _ptr(ws13), _ptr(ws2), wdt, _ptr(out))
+    return out
+
+
+def combine(y: np.ndarray, y_sh: np.ndarray | None, inv_row: np.ndarray,
+            gate: np.ndarray) -> np.ndarray:
+    """fp64 [T,H] = y_sh + sum of gate-weighted rows of y (dropped = -1)."""
+    y = np.ascontiguousarray(y)
+    inv_row = np.ascontiguousarray(inv_row, dtype=np.int32)
+    T, k = inv_row.shape
+    H = y.shape[1]
+    if y_sh is not None:
+        y_sh = np.ascontiguousarray(y_sh)
+        assert y_sh.dtype == y.dtype and y_sh.shape == (T, H)
+    g = np.ascontiguousarray(gate, dtype=np.float64)
+    out = np.empty((T, H), np.float64)
+    lib().orc_combine(T, H, k, _ptr(y), _ptr(y_sh), _typed(y), _ptr(inv_row), _ptr(g), _ptr(out))
     return out
 
 

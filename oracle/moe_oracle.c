@@ -339,6 +339,20 @@ void orc_token_output(int H, int k, int I, int n_shared, int I_sh,
   }
 }
 
+void orc_combine(int T, int H, int k, const void* y, const void* y_sh, int dtype,
+                 const int32_t* inv_row, const double* gate, double* out) {
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < H; ++h) {
+      double acc = y_sh ? typed_at(y_sh, dtype, (int64_t)t * H + h) : 0.0;
+      for (int j = 0; j < k; ++j) {
+        int r = inv_row[(int64_t)t * k + j];
+        if (r < 0) continue;
+        acc += gate[(int64_t)t * k + j] * typed_at(y, dtype, (int64_t)r * H + h);
+      }
+      out[(int64_t)t * H + h] = acc;
+    }
+}
+
 /* ---------------------------------------------------------------- stats */
 
 void orc_load_stats(int T, int N, int k, int score_fn, const float* logits,

@@ -104,6 +104,13 @@ void orc_token_output(int H, int k, int I, int n_shared, int I_sh,
                       const double* gates, const void* ws13, const void* ws2,
                       int w_dtype, double* out);
 
+/* Combine ([BUILD] §2.2 shared + routed; [EVO] §GShard dropped slots add
+ * nothing): out[t] = y_sh[t] + sum_{j<k, inv_row[t,j] >= 0} gate[t,j] *
+ * y[inv_row[t,j]].  y (typed) [*,H], y_sh (typed) [T,H] or NULL,
+ * gate [T,k] fp64; out [T,H] fp64. */
+void orc_combine(int T, int H, int k, const void* y, const void* y_sh, int dtype,
+                 const int32_t* inv_row, const double* gate, double* out);
+
 /* Load statistics ([EVO] §ST-MoE): f_e = c_e/(k T),
  * P_e = sum_t s[t,e] / sum_t sum_e' s[t,e'], L_B = N sum_e f_e P_e,
  * z = (1/T) sum_t LSE(l_t), z_sq = (1/T) sum_t LSE(l_t)^2.

@@ -1,0 +1,339 @@
+// dispatch.hip -- per-expert histogram, prefix sums, capacity drop and the
+// token permutation, all deterministic (no order-dependent atomics).
+//
+// Sources: "DeepSeek MoE：从v1到v3的演进" §GShard (tokens are sent to the
+// experts that own them; expert capacity; overflow passes through the
+// residual) and §DeepSeek-v2 (the lowest-scored tokens are the ones dropped).
+//
+// Rows are laid out expert by expert, ascending token order inside an
+// expert.  A token's rank inside its expert comes from LDS bit masks: wave w
+// of a block ORs bit `lane` into mask[w][e] for each expert its token chose;
+// OR is order-independent, and popcounts of the masks below a lane give the
+// number of earlier tokens of the block that chose e.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
+
+int dispatch_blocks(int T) { return (T + kTokPerBlock - 1) / kTokPerBlock; }
+
+static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t dispatch_ws_bytes(int T, int N, int k, int capacity) {
+  const size_t nb = dispatch_blocks(T);
+  size_t b = 0;
+  b += align256(nb * N * sizeof(int32_t));  // block_counts
+  b += align256(nb * N * sizeof(int32_t));  // block_base
+  b += align256(N * sizeof(int32_t));       // pre_off
+  if (capacity > 0) {
+    b += align256(static_cast<size_t>(T) * k * sizeof(uint64_t));
+    b += align256(static_cast<size_t>(T) * k * sizeof(int32_t));
+  }
+  return b;
+}
+
+DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, int capacity) {
+  const size_t nb = dispatch_blocks(T);
+  char* p = static_cast<char*>(ws);
+  DispatchWs w{};
+  w.block_counts = reinterpret_cast<int32_t*>(p);
+  p += align256(nb * N * sizeof(int32_t));
+  w.block_base = reinterpret_cast<int32_t*>(p);
+  p += align256(nb * N * sizeof(int32_t));
+  w.pre_off = reinterpret_cast<int32_t*>(p);
+  p += align256(N * sizeof(int32_t));
+  if (capacity > 0) {
+    w.cand_key = reinterpret_cast<uint64_t*>(p);
+    p += align256(static_cast<size_t>(T) * k * sizeof(uint64_t));
+    w.cand_slot = reinterpret_cast<int32_t*>(p);
+  }
+  return w;
+}
+
+// Build mask[w][e] for this block's tokens.  masks: [4][N] in LDS.
+__device__ __forceinline__ void build_masks(unsigned long long* masks,
+                                            const int32_t* __restrict__ topk_idx, int T,
+                                            int N, int k) {
+  for (int i = threadIdx.x; i < 4 * N; i += blockDim.x) masks[i] = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * kTokPerBlock + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[static_cast<int64_t>(t) * k + j];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N))
+        atomicOr(&masks[w * N + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ topk_idx,
+                                                             int T, int N, int k,
+                                                             int32_t* __restrict__ block_counts) {
+  extern __shared__ unsigned long long masks[];
+  build_masks(masks, topk_idx, T, N, k);
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c += __popcll(masks[w * N + e]);
+    block_counts[static_cast<int64_t>(blockIdx.x) * N + e] = c;
+  }
+}
+
+// Inclusive scan of one value per thread over a 256-thread block.
+__device__ __forceinline__ int block_scan_incl(int v, int* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int a = threadIdx.x >= o ? sh[threadIdx.x - o] : 0;
+    __syncthreads();
+    sh[threadIdx.x] += a;
+    __syncthreads();
+  }
+  int r = sh[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+// One block of 256 threads; thread e owns expert e (N <= 256).
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ block_counts,
+                                                            int nb, int N, int capacity,
+                                                            int32_t* __restrict__ block_base,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ pre_off,
+                                                            int32_t* __restrict__ n_dropped) {
+  __shared__ int sh[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < N) {
+    for (int b = 0; b < nb; ++b) {
+      const int64_t o = static_cast<int64_t>(b) * N + e;
+      const int c = block_counts[o];
+      block_base[o] = run;
+      run += c;
+    }
+  }
+  const int c_e = e < N ? run : 0;
+  const int kept = (capacity > 0 && c_e > capacity) ? capacity : c_e;
+  const int incl_c = block_scan_incl(c_e, sh);
+  const int incl_k = block_scan_incl(kept, sh);
+  const int drop_tot = block_scan_incl(c_e - kept, sh);
+  if (e < N) {
+    counts[e] = c_e;
+    pre_off[e] = incl_c - c_e;
+    offsets[e] = incl_k - kept;
+  }
+  if (e == N - 1) {
+    offsets[N] = incl_k;
+    if (n_dropped) {
+      n_dropped[0] = drop_tot;
+      n_dropped[1] = 0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score, int T, int N,
+    int k, int capacity, const int32_t* __restrict__ block_base,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pre_off, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ inv_row, uint64_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_slot) {
+  extern __shared__ unsigned long long masks[];
+  build_masks(masks, topk_idx, T, N, k);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * kTokPerBlock + threadIdx.x;
+  if (t >= T) return;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j = 0; j < k; ++j) {
+    const int64_t slot = static_cast<int64_t>(t) * k + j;
+    const int e = topk_idx[slot];
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(N)) {  // outside the contract
+      inv_row[slot] = -1;
+      continue;
+    }
+    int rank = block_base[static_cast<int64_t>(blockIdx.x) * N + e];
+    for (int w2 = 0; w2 < w; ++w2) rank += __popcll(masks[w2 * N + e]);
+    rank += __popcll(masks[w * N + e] & below);
+    if (capacity == 0 || counts[e] <= capacity) {
+      const int row = offsets[e] + rank;
+      inv_row[slot] = row;
+      row_token[row] = t;
+    } else {
+      const int pos = pre_off[e] + rank;
+      cand_key[pos] = (static_cast<uint64_t>(f32_order_key(topk_score[slot])) << 32) |
+                      (0xffffffffu - static_cast<uint32_t>(t));
+      cand_slot[pos] = static_cast<int32_t>(slot);
+    }
+  }
+}
+
+// One workgroup per expert over capacity.  Finds the capacity-th largest
+// 64-bit key (score order key, then lower token) by an 8-bit radix select,
+// then keeps every key >= it, in token order.
+constexpr int kCapThreads = 1024;
+
+__global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pre_off, const uint64_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_slot, int k, int capacity,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ inv_row) {
+  const int e = blockIdx.x;
+  const int c = counts[e];
+  if (c <= capacity) return;  // uniform
+  __shared__ int hist[256];
+  __shared__ unsigned long long sh_prefix;
+  __shared__ int sh_need;
+  __shared__ int scan[kCapThreads];
+  const uint64_t* keys = cand_key + pre_off[e];
+  const int32_t* slots = cand_slot + pre_off[e];
+
+  if (threadIdx.x == 0) {
+    sh_prefix = 0ull;
+    sh_need = capacity;
+  }
+  for (int d = 7; d >= 0; --d) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const uint64_t prefix = sh_prefix;
+    const int hs = 8 * (d + 1);
+    for (int i = threadIdx.x; i < c; i += blockDim.x) {
+      const uint64_t key = keys[i];
+      const bool match = (d == 7) || ((key >> hs) == (prefix >> hs));
+      if (match) atomicAdd(&hist[(key >> (8 * d)) & 255], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int need = sh_need;
+      int cum = 0;
+      int digit = 0;
+      for (int v = 255; v >= 0; --v) {
+        if (cum + hist[v] >= need) {
+          digit = v;
+          break;
+        }
+        cum += hist[v];
+      }
+      sh_need = need - cum;
+      sh_prefix = prefix | (static_cast<uint64_t>(digit) << (8 * d));
+    }
+    __syncthreads();
+  }
+  const uint64_t tau = sh_prefix;
+
+  // keep keys >= tau (exactly `capacity` of them: keys are distinct)
+  const int base_row = offsets[e];
+  int running = 0;
+  for (int c0 = 0; c0 < c; c0 += kCapThreads) {
+    const int i = c0 + threadIdx.x;
+    const int keep = (i < c && keys[i] >= tau) ? 1 : 0;
+    scan[threadIdx.x] = keep;
+    __syncthreads();
+    for (int o = 1; o < kCapThreads; o <<= 1) {
+      const int a = threadIdx.x >= o ? scan[threadIdx.x - o] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += a;
+      __syncthreads();
+    }
+    const int excl = scan[threadIdx.x] - keep;
+    const int chunk_total = scan[kCapThreads - 1];
+    if (i < c) {
+      const int slot = slots[i];
+      if (keep) {
+        const int row = base_row + running + excl;
+        inv_row[slot] = row;
+        row_token[row] = slot / k;
+      } else {
+        inv_row[slot] = -1;
+      }
+    }
+    running += chunk_total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void count_all_dropped_kernel(const int32_t* __restrict__ inv_row,
+                                                                int T, int k,
+                                                                int32_t* __restrict__ n_dropped) {
+  __shared__ int sh[4];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int flag = 0;
+  if (t < T) {
+    flag = 1;
+    for (int j = 0; j < k; ++j) flag &= (inv_row[static_cast<int64_t>(t) * k + j] < 0);
+  }
+  int s = flag;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int tot = sh[0] + sh[1] + sh[2] + sh[3];
+    if (tot) atomicAdd(&n_dropped[1], tot);  // integer sum: order-independent
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
+                           int k, int capacity, int32_t* counts, int32_t* offsets,
+                           int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
+                           const DispatchWs& w, hipStream_t st) {
+  const int nb = dispatch_blocks(T);
+  const size_t lds = 4 * N * sizeof(unsigned long long);
+  if (nb > 0 && k > 0)
+    dispatch_count_kernel<<<nb, 256, lds, st>>>(topk_idx, T, N, k, w.block_counts);
+  else if (nb > 0)
+    fill_i32_kernel<<<(nb * N + 255) / 256, 256, 0, st>>>(w.block_counts, nb * N, 0);
+  dispatch_scan_kernel<<<1, 256, 0, st>>>(w.block_counts, nb, N, capacity, w.block_base,
+                                          counts, offsets, w.pre_off, n_dropped);
+  if (nb > 0 && k > 0) {
+    dispatch_scatter_kernel<<<nb, 256, lds, st>>>(topk_idx, topk_score, T, N, k, capacity,
+                                                  w.block_base, counts, offsets, w.pre_off,
+                                                  row_token, inv_row, w.cand_key, w.cand_slot);
+    if (capacity > 0) {
+      capacity_select_kernel<<<N, kCapThreads, 0, st>>>(counts, offsets, w.pre_off, w.cand_key,
+                                                        w.cand_slot, k, capacity, row_token,
+                                                        inv_row);
+      if (n_dropped)
+        count_all_dropped_kernel<<<(T + 255) / 256, 256, 0, st>>>(inv_row, T, k, n_dropped);
+    }
+  }
+  return hipGetLastError();
+}
+
+// x_perm[r] = x[row_token[r]] for r < offsets[N]; one wave per row, 16-byte
+// vectors.
+__global__ __launch_bounds__(256) void permute_kernel(const char* __restrict__ x,
+                                                      int64_t row_bytes,
+                                                      const int32_t* __restrict__ row_token,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int N, char* __restrict__ x_perm) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= offsets[N]) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(row_token[r]) * row_bytes);
+  u32x4* dst = reinterpret_cast<u32x4*>(x_perm + static_cast<int64_t>(r) * row_bytes);
+  const int nv = static_cast<int>(row_bytes / 16);
+  for (int i = lane; i < nv; i += 64) dst[i] = src[i];
+}
+
+hipError_t launch_permute(const void* x, int elem_bytes, int H, const int32_t* row_token,
+                          const int32_t* offsets, int N, int max_rows, void* x_perm,
+                          hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  permute_kernel<<<(max_rows + 3) / 4, 256, 0, st>>>(
+      static_cast<const char*>(x), static_cast<int64_t>(H) * elem_bytes, row_token, offsets, N,
+      static_cast<char*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

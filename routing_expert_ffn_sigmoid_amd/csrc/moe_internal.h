@@ -1,0 +1,179 @@
+// moe_internal.h -- device helpers and kernel-launcher declarations shared by
+// the translation units of libmoe.so (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits in global memory
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// Wave-wide butterfly reductions (64 lanes).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of an fp32 value to uint32 (larger float -> larger
+// integer); -0 is folded onto +0 so the two compare equal, as floats do.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------------ fp32 sigmoid
+// The score every selection is made on, so it is defined exactly:
+//   x = clamp(-l, -87, 87); n = rne(fl32(x * log2 e));
+//   r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r)     (Cody & Waite, with
+//       fdlibm's two-part ln 2);
+//   p = sum_{j<=7} r^j/j! by fma Horner; E = p * 2^n; s = 1 / (1 + E)
+// with correctly rounded fp32 add and divide.  The clamp keeps every result
+// a normal fp32 number (s saturates at sigma(-87) below l = -87).
+__device__ __forceinline__ float sigmoid_score(float l) {
+#pragma clang fp contract(off)
+  float x = __builtin_fminf(__builtin_fmaxf(-l, -87.0f), 87.0f);
+  const float n = __builtin_rintf(x * 0x1.715476p+0f);
+  float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
+  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+  float p = 1.0f / 5040.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const float e = __builtin_ldexpf(p, static_cast<int>(n));
+  const float d = 1.0f + e;
+  return 1.0f / d;
+}
+
+// ------------------------------------------------------------------ launchers
+// Every launcher enqueues on `st` and returns hipGetLastError().
+
+// logits partials: part[s][t][e] = sum over split s of x[t,h] * wg[e,h].
+hipError_t launch_router_gemm(const void* x, int x_dtype, const void* wg, int wg_dtype,
+                              float* part, int T, int H, int N, int splits, hipStream_t st);
+int router_splits(int T, int H, int N);
+
+struct RouteParams {
+  const float* part;  // [splits][T][N] logit partials (or the logits, splits = 1)
+  int splits;
+  float* logits;      // [T][N] out (may equal part when splits == 1)
+  const float* bias;  // [N] or null
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* topk_score;
+  float* token_lse;   // may be null
+  int T, N, k, n_groups, topk_groups, group_topn, score_fn, norm_topk;
+  float route_scale;
+};
+hipError_t launch_route(const RouteParams& p, hipStream_t st);
+
+struct DispatchWs {
+  int32_t* block_counts;  // [nb][N]
+  int32_t* block_base;    // [nb][N]
+  int32_t* pre_off;       // [N]
+  uint64_t* cand_key;     // [T*k] (capacity only)
+  int32_t* cand_slot;     // [T*k] (capacity only)
+};
+int dispatch_blocks(int T);
+size_t dispatch_ws_bytes(int T, int N, int k, int capacity);
+DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, int capacity);
+hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
+                           int k, int capacity, int32_t* counts, int32_t* offsets,
+                           int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
+                           const DispatchWs& w, hipStream_t st);
+hipError_t launch_permute(const void* x, int elem_bytes, int H, const int32_t* row_token,
+                          const int32_t* offsets, int N, int max_rows, void* x_perm,
+                          hipStream_t st);
+
+// One problem group of the grouped SwiGLU GEMM.
+struct FfnGroup {
+  const void* A;            // activations [*, lda]
+  int64_t lda;
+  const int32_t* row_index; // optional gather: problem row r reads A[row_index[r]]
+  const int32_t* seg_off;   // [nseg+1] device, or null = one segment of `rows`
+  int32_t nseg;
+  int32_t rows;             // used when seg_off == null
+  const void* W;            // weights, segment s at W + s * w_stride (elements)
+  int64_t w_stride;
+  void* Out;                // [*, ldo]
+  int64_t ldo;
+  int32_t K;                // reduction length
+  int32_t n_out;            // output columns (h cols in the gate/up phase)
+  int32_t up_off;           // gate/up phase: row offset of the up half (= inter)
+};
+// phase 0: gate/up + SwiGLU -> h;  phase 1: down projection -> y.
+// `rows_hint`: expected rows per segment (chooses the tile height).
+hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int rows_hint,
+                           hipStream_t st);
+hipError_t launch_ffn_f32(const FfnGroup& g, int phase, int max_rows, hipStream_t st);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* inv_row, const float* gate,
+                          const void* y_shared, void* out, int T, int H, int k,
+                          int act_dtype, hipStream_t st);
+
+int stats_blocks(int T);
+size_t stats_ws_bytes(int T, int N);
+hipError_t launch_stats(const int32_t* counts, const float* lse, const float* logits, int T,
+                        int N, int k, int score_fn, float* f, float* P, float* scalars,
+                        void* ws, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int N, float u,
+                              hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+"""Shared helpers of the GPU parity tests: tensors <-> oracle arrays, the
+normwise error measures and one-call drivers of the HIP library."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_expert_ffn_sigmoid_amd as moe
+from routing_expert_ffn_sigmoid_amd import synth, workloads
+
+BF16_MAXREL, BF16_RELL2 = 2e-2, 5e-3   # bf16 paths vs fp32-or-better oracle
+F32_MAXREL = 1e-5                      # fp32 paths
+
+gpu = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def typed(t: torch.Tensor) -> np.ndarray:
+    """Tensor -> oracle typed array (fp32, or raw bf16 bits as uint16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.to(torch.float32).numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def normwise(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    den_inf = np.max(np.abs(ref)) if ref.size else 0.0
+    den_l2 = np.linalg.norm(ref)
+    maxrel = float(np.max(np.abs(d)) / den_inf) if den_inf > 0 else float(np.max(np.abs(d), initial=0))
+    rell2 = float(np.linalg.norm(d) / den_l2) if den_l2 > 0 else float(np.linalg.norm(d))
+    return maxrel, rell2
+
+
+def score_fn_const(wl) -> int:
+    return oracle.SIGMOID if wl.score_fn == workloads.SIGMOID else oracle.SOFTMAX
+
+
+def oracle_route(wl, logits_np, bias_np):
+    return oracle.route(logits_np, bias_np, wl.k, wl.n_groups, wl.topk_groups, wl.group_topn,
+                        score_fn_const(wl), wl.norm_topk, wl.route_scale)
+
+
+def layer_forward(wl, inp, ws=None, aux=None, cfg=None):
+    cfg = cfg or moe.make_cfg(wl)
+    dt = torch.bfloat16 if wl.act_dtype == workloads.BF16 else torch.float32
+    out = torch.empty((wl.T, wl.H), dtype=dt, device="cuda")
+    if aux is None:
+        aux = moe.alloc_aux(cfg)
+    if ws is None:
+        ws = moe.alloc_workspace(cfg)
+    weights = {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")}
+    moe.moe_layer_forward(cfg, weights, inp["x"], inp["bias"], out, aux, ws)
+    torch.cuda.synchronize()
+    return out, aux
+
+
+def check_routing(wl, aux, bias):
+    """Bit-exact selection given the GPU's fp32 logits; gates/lse to 1e-5."""
+    logits = aux["logits"].cpu().numpy()
+    b = bias.cpu().numpy() if bias is not None else None
+    r = oracle_route(wl, logits, b)
+    got_idx = aux["topk_idx"].cpu().numpy()
+    mism = np.argwhere(got_idx != r["topk_idx"])
+    assert mism.size == 0, f"{len(mism)} expert-index mismatches, first at {mism[:3].tolist()}"
+    if wl.score_fn == workloads.SIGMOID:
+        np.testing.assert_array_equal(aux["topk_score"].cpu().numpy(), r["topk_score"])
+    mr, _ = normwise(aux["topk_gate"].cpu().numpy(), r["topk_gate"])
+    assert mr <= F32_MAXREL, f"gate max-rel {mr}"
+    mr, _ = normwise(aux["token_lse"].cpu().numpy(), r["lse"])
+    assert mr <= F32_MAXREL, f"lse max-rel {mr}"
+    return r
+
+
+def check_dispatch(wl, aux, r):
+    d = oracle.dispatch(r["topk_idx"], r["topk_score"], wl.N, wl.capacity)
+    np.testing.assert_array_equal(aux["counts"].cpu().numpy(), d["counts"])
+    np.testing.assert_array_equal(aux["offsets"].cpu().numpy(), d["offsets"])
+    M = int(d["offsets"][-1])
+    np.testing.assert_array_equal(aux["row_token"].cpu().numpy()[:M], d["row_token"])
+    np.testing.assert_array_equal(aux["inv_row"].cpu().numpy(), d["inv_row"])
+    nd = aux["n_dropped"].cpu().numpy()
+    assert int(nd[0]) == d["n_dropped"] and int(nd[1]) == d["n_tok_all_dropped"]
+    return d
+
+
+def check_stats(wl, aux):
+    st = oracle.load_stats(aux["logits"].cpu().numpy(), aux["counts"].cpu().numpy(), wl.k,
+                           score_fn_const(wl))
+    for name, ref in (("f", st["f"]), ("P", st["P"])):
+        mr, _ = normwise(aux[name].cpu().numpy(), ref)
+        assert mr <= F32_MAXREL, f"{name} max-rel {mr}"
+    sc = aux["scalars"].cpu().numpy().astype(np.float64)
+    for i, key in enumerate(("L_B", "z", "z_sq")):
+        assert abs(sc[i] - st[key]) <= F32_MAXREL * max(1.0, abs(st[key])), (key, sc[i], st[key])
+    return st
+
+
+def oracle_rows(wl, inp, r, d, tokens):
+    """Oracle layer output (fp64) for the given tokens."""
+    x = inp["x"]
+    ws13 = typed(inp["ws13"]) if inp.get("ws13") is not None else None
+    ws2 = typed(inp["ws2"]) if inp.get("ws2") is not None else None
+    cache13, cache2 = {}, {}
+
+    def expert(e):
+        if e not in cache13:
+            cache13[e] = typed(inp["w13"][e])
+            cache2[e] = typed(inp["w2"][e])
+        return cache13[e], cache2[e]
+
+    rows = []
+    for t in tokens:
+        w13s, w2s = [], []
+        for j in range(wl.k):
+            if d["inv_row"][t, j] < 0:
+                w13s.append(None)
+                w2s.append(None)
+            else:
+                a, b = expert(int(r["topk_idx"][t, j]))
+                w13s.append(a)
+                w2s.append(b)
+        rows.append(oracle.token_output(typed(x[t]), w13s, w2s, r["topk_gate"][t], ws13, ws2,
+                                        wl.n_shared, wl.I_shared, wl.I))
+    return np.stack(rows)
+
+
+def check_outputs(wl, out, ref_rows, tokens):
+    got = f64(out[tokens])
+    mr, l2 = normwise(got, ref_rows)
+    if wl.act_dtype == workloads.BF16:
+        assert mr <= BF16_MAXREL and l2 <= BF16_RELL2, f"max-rel {mr:.3e} rel-L2 {l2:.3e}"
+    else:
+        assert mr <= F32_MAXREL, f"max-rel {mr:.3e}"
+    return mr, l2
+
+
+def make_inputs(wl, device="cuda"):
+    return synth.make_inputs(wl, device=device)

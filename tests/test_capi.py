@@ -1,0 +1,118 @@
+"""Host-only checks of the C ABI (no GPU needed): every symbol moe.h declares
+is exported by libmoe.so, and invalid arguments are rejected on the host with
+the documented status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_expert_ffn_sigmoid_amd as moe
+from routing_expert_ffn_sigmoid_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                               reason="libmoe.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_load_stats",
+              "moe_layer_forward", "moe_workspace_size", "moe_status_string"]:
+        assert n in names
+    assert set(names) == set(moe.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), f"libmoe.so does not export {n}"
+
+
+@needs_lib
+def test_status_strings():
+    for code in range(5):
+        assert moe.status_string(code).startswith("MOE_")
+
+
+def _ws_size(cfg):
+    n = ctypes.c_size_t(0)
+    return moe.lib().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), n.value
+
+
+@needs_lib
+@pytest.mark.parametrize("name", list(workloads.SHORT))
+def test_workspace_size_for_presets(name):
+    cfg = moe.make_cfg(workloads.get(name))
+    rc, n = _ws_size(cfg)
+    assert rc == moe.MOE_OK and n > 0
+
+
+@needs_lib
+@pytest.mark.parametrize("override,code", [
+    ({"N": 0}, moe.MOE_ERR_INVALID_ARG),
+    ({"T": -1}, moe.MOE_ERR_INVALID_ARG),
+    ({"n_groups": 3}, moe.MOE_ERR_INVALID_ARG),          # 3 does not divide 16
+    ({"topk_groups": 5}, moe.MOE_ERR_INVALID_ARG),
+    ({"k": 9}, moe.MOE_ERR_INVALID_ARG),                  # > 2 kept groups x 4 experts
+    ({"group_topn": 3}, moe.MOE_ERR_INVALID_ARG),
+    ({"score_fn": 7}, moe.MOE_ERR_INVALID_ARG),
+    ({"capacity": -1}, moe.MOE_ERR_INVALID_ARG),
+    ({"act_dtype": 5}, moe.MOE_ERR_INVALID_ARG),
+    ({"N": 260, "n_groups": 4}, moe.MOE_ERR_UNSUPPORTED),
+    ({"N": 18, "n_groups": 1, "topk_groups": 1}, moe.MOE_ERR_UNSUPPORTED),
+    ({"H": 100}, moe.MOE_ERR_UNSUPPORTED),
+    ({"I": 96}, moe.MOE_ERR_UNSUPPORTED),
+    ({"N": 16, "n_groups": 8, "topk_groups": 2}, moe.MOE_ERR_UNSUPPORTED),  # groups of 2
+    ({"w_dtype": 1}, moe.MOE_ERR_UNSUPPORTED),
+    ({"score_fn": 0, "capacity": 4}, moe.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_configs_rejected_on_host(override, code):
+    cfg = moe.make_cfg(workloads.TINY, **override)
+    rc, _ = _ws_size(cfg)
+    assert rc == code
+    # the layer entry point rejects the same configuration before any launch
+    w = moe.MoeWeights()
+    rc2 = moe.lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), None, None, None,
+                                      None, None, 0, None)
+    assert rc2 == code
+
+
+@needs_lib
+def test_missing_workspace_and_pointers_rejected():
+    cfg = moe.make_cfg(workloads.TINY)
+    w = moe.MoeWeights()
+    L = moe.lib()
+    # NULL x / out with T > 0
+    assert L.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), None, None, None, None,
+                               None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    # all pointers present (never dereferenced), workspace too small
+    fake = ctypes.c_void_p(0x1000)
+    w = moe.MoeWeights(fake, fake, fake, fake, fake)
+    assert L.moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), fake, None, fake, None,
+                               fake, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_load_stats(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, None, 0,
+                            None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_permute(ctypes.byref(cfg), fake, fake, None, fake, fake, fake, fake, None,
+                         None, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_ffn(ctypes.byref(cfg), 0, None, 4, 64, fake, None, fake, fake, fake,
+                             fake, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(cfg), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(None, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(moe, "_LIB", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()

@@ -1,0 +1,269 @@
+"""GPU parity of every entry point at sizes the oracle finishes in seconds,
+with ragged tails, empty segments, ties, drops and degenerate shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_expert_ffn_sigmoid_amd as moe
+from routing_expert_ffn_sigmoid_amd import synth, workloads
+
+from gpu_common import (BF16_MAXREL, BF16_RELL2, F32_MAXREL, check_dispatch, check_outputs,
+                        check_routing, check_stats, f64, gpu, layer_forward, make_inputs,
+                        normwise, oracle_route, oracle_rows, require_gpu, say, typed)
+
+pytestmark = gpu
+
+
+def _route_only(wl, logits, bias):
+    cfg = moe.make_cfg(wl)
+    T, k = wl.T, wl.k
+    dev = "cuda"
+    lg = logits.clone()
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    score = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    moe.moe_route(cfg, None, None, lg, bias, idx, gate, score, lse)
+    torch.cuda.synchronize()
+    return dict(logits=lg, topk_idx=idx, topk_gate=gate, topk_score=score, token_lse=lse)
+
+
+def test_sigmoid_scores_bit_identical_to_oracle_on_a_sweep():
+    """All 64 scores of each token are returned (k = N = 64, no groups), so the
+    GPU's fp32 sigmoid is compared bit for bit with the oracle's."""
+    require_gpu()
+    vals = np.concatenate([
+        np.linspace(-90, 90, 1 << 20, dtype=np.float32),
+        np.arange(0, 0x42B40000, 4099, dtype=np.uint32).view(np.float32),
+    ])
+    vals = np.concatenate([vals, -vals])
+    n = (vals.size // 64) * 64
+    logits = torch.from_numpy(vals[:n].reshape(-1, 64).copy()).cuda()
+    wl = workloads.TINY.with_(T=logits.shape[0], N=64, k=64, n_groups=1, topk_groups=1,
+                              norm_topk=0)
+    say(f"sigmoid sweep: {n} values")
+    g = _route_only(wl, logits, None)
+    r = oracle_route(wl, logits.cpu().numpy(), None)
+    np.testing.assert_array_equal(g["topk_idx"].cpu().numpy(), r["topk_idx"])
+    np.testing.assert_array_equal(g["topk_score"].cpu().numpy(), r["topk_score"])
+
+
+@pytest.mark.parametrize("G,keep,k,topn", [(4, 2, 4, 2), (4, 1, 3, 1), (2, 1, 5, 2), (1, 1, 6, 2)])
+@pytest.mark.parametrize("fn", [workloads.SIGMOID, workloads.SOFTMAX])
+def test_route_ties_match_oracle(G, keep, k, topn, fn):
+    """Integer-valued keys with many ties: ties must resolve to the lower
+    group / expert index exactly as in the oracle."""
+    require_gpu()
+    rng = np.random.default_rng(G * 100 + k * 10 + topn + fn)
+    T, N = 333, 16
+    if fn == workloads.SIGMOID:
+        logits = np.zeros((T, N), np.float32)  # every score exactly 0.5
+        bias = rng.integers(-2, 3, size=N).astype(np.float32)
+        # vary keys per token through the logit: l = 0 or a large value
+        logits = (rng.integers(0, 2, size=(T, N)) * 30.0).astype(np.float32)
+    else:
+        logits = rng.integers(-3, 4, size=(T, N)).astype(np.float32)
+        bias = None
+    wl = workloads.TINY.with_(T=T, N=N, k=k, n_groups=G, topk_groups=keep, group_topn=topn,
+                              score_fn=fn, norm_topk=1 if fn == workloads.SIGMOID else 0)
+    say(f"ties: G={G} keep={keep} k={k} topn={topn} fn={fn}")
+    bt = torch.from_numpy(bias).cuda() if bias is not None else None
+    g = _route_only(wl, torch.from_numpy(logits).cuda(), bt)
+    r = oracle_route(wl, logits, bias)
+    np.testing.assert_array_equal(g["topk_idx"].cpu().numpy(), r["topk_idx"])
+    mr, _ = normwise(g["topk_gate"].cpu().numpy(), r["topk_gate"])
+    assert mr <= F32_MAXREL
+
+
+def test_uniform_routing_balance_loss_is_one_on_gpu():
+    """Construction with exactly uniform routing: L_B = 1 within fp32."""
+    require_gpu()
+    T, N, k = 64, 16, 4
+    logits = np.full((T, N), -1000.0, np.float32)
+    for t in range(T):
+        for j in range(k):
+            logits[t, (4 * t + j) % N] = 0.0
+    wl = workloads.TINY.with_(T=T, N=N, k=k, n_groups=1, topk_groups=1, score_fn=workloads.SOFTMAX,
+                              norm_topk=0)
+    cfg = moe.make_cfg(wl)
+    g = _route_only(wl, torch.from_numpy(logits).cuda(), None)
+    ws = moe.alloc_workspace(cfg)
+    counts = torch.empty(N, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(N + 1, dtype=torch.int32, device="cuda")
+    rt = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    moe.moe_permute(cfg, g["topk_idx"], g["topk_score"], None, counts, offsets, rt, inv, ws=ws)
+    f = torch.empty(N, device="cuda")
+    P = torch.empty(N, device="cuda")
+    sc = torch.empty(3, device="cuda")
+    moe.moe_load_stats(cfg, counts, g["token_lse"], g["logits"], f, P, sc, ws)
+    torch.cuda.synchronize()
+    assert np.all(counts.cpu().numpy() == T * k // N)
+    assert abs(float(sc[0]) - 1.0) <= 1e-6
+    assert abs(float(sc[1]) - np.log(4)) <= 1e-6
+
+
+@pytest.mark.parametrize("T", [64, 77, 1, 300])
+def test_tiny_layer_full_parity(T):
+    """fp32 tiny layer: every output row against the oracle at 1e-5."""
+    require_gpu()
+    wl = workloads.TINY.with_(T=T)
+    say(f"tiny layer T={T}")
+    inp = make_inputs(wl)
+    out, aux = layer_forward(wl, inp)
+    r = check_routing(wl, aux, inp["bias"])
+    d = check_dispatch(wl, aux, r)
+    check_stats(wl, aux)
+    toks = list(range(T))
+    ref = oracle_rows(wl, inp, r, d, toks)
+    mr, _ = check_outputs(wl, out, ref, toks)
+    say(f"  max-rel {mr:.2e}")
+
+
+@pytest.mark.parametrize("C", [1, 3, 17])
+def test_tiny_layer_with_capacity_drops(C):
+    require_gpu()
+    wl = workloads.TINY.with_(T=200, capacity=C)
+    say(f"tiny capacity C={C}")
+    inp = make_inputs(wl)
+    out, aux = layer_forward(wl, inp)
+    r = check_routing(wl, aux, inp["bias"])
+    d = check_dispatch(wl, aux, r)
+    assert d["n_dropped"] > 0
+    toks = list(range(wl.T))
+    ref = oracle_rows(wl, inp, r, d, toks)
+    check_outputs(wl, out, ref, toks)
+
+
+def test_shared_only_and_empty_batch():
+    require_gpu()
+    wl = workloads.TINY.with_(k=0)
+    inp = make_inputs(wl)
+    out, aux = layer_forward(wl, inp)
+    r = check_routing(wl, aux, inp["bias"])
+    d = check_dispatch(wl, aux, r)
+    ref = oracle_rows(wl, inp, r, d, list(range(wl.T)))
+    check_outputs(wl, out, ref, list(range(wl.T)))
+    wl0 = workloads.TINY.with_(T=0)
+    inp0 = make_inputs(wl0)
+    out0, aux0 = layer_forward(wl0, inp0)
+    assert out0.numel() == 0 and int(aux0["offsets"][-1]) == 0
+
+
+def test_bf16_small_layer_parity_and_determinism():
+    """A small bf16 V3-like layer (groups, sigmoid, scale 2.5) exercising the
+    MFMA path with ragged segments."""
+    require_gpu()
+    wl = workloads.V3_PREFILL.with_(T=333, H=256, N=32, k=4, n_groups=4, topk_groups=2, I=128,
+                                    I_shared=192)
+    say("bf16 small layer")
+    inp = make_inputs(wl)
+    out, aux = layer_forward(wl, inp)
+    r = check_routing(wl, aux, inp["bias"])
+    d = check_dispatch(wl, aux, r)
+    check_stats(wl, aux)
+    toks = list(range(0, wl.T, 7))
+    ref = oracle_rows(wl, inp, r, d, toks)
+    mr, l2 = check_outputs(wl, out, ref, toks)
+    say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
+    out2, aux2 = layer_forward(wl, inp)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    for n in ("topk_idx", "topk_gate", "row_token", "inv_row", "f", "P", "scalars"):
+        assert torch.equal(aux[n], aux2[n]), n
+
+
+@pytest.mark.parametrize("rows_per_seg", [5, 40, 150])
+def test_grouped_ffn_ragged_segments(rows_per_seg):
+    """moe_grouped_ffn alone: ragged and empty segments, every tile height."""
+    require_gpu()
+    rng = np.random.default_rng(rows_per_seg)
+    nseg, H, inter = 9, 256, 192
+    sizes = rng.integers(0, 2 * rows_per_seg, size=nseg)
+    sizes[2] = 0
+    sizes[5] = 3 * rows_per_seg + 7
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offs[-1])
+    wl = workloads.V3_PREFILL.with_(H=H, N=16, n_groups=1, topk_groups=1, k=2, I=64)
+    cfg = moe.make_cfg(wl)
+    say(f"grouped ffn: sizes={sizes.tolist()}")
+    a = synth.normal((M, H), 1.0, torch.bfloat16, "cuda", 1, "a")
+    w13 = synth.normal((nseg, 2 * inter, H), 0.02, torch.bfloat16, "cuda", 1, "w13")
+    w2 = synth.normal((nseg, H, inter), 0.02, torch.bfloat16, "cuda", 1, "w2")
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_grouped_ffn_workspace_size(cfg, M, inter), dtype=torch.uint8,
+                     device="cuda")
+    moe.moe_grouped_ffn(cfg, nseg, torch.from_numpy(offs).cuda(), M, inter, a, None, w13, w2,
+                        y, ws)
+    torch.cuda.synchronize()
+    ref = np.empty((M, H))
+    an = typed(a)
+    w13n, w2n = typed(w13), typed(w2)
+    for s in range(nseg):
+        for r_ in range(offs[s], offs[s + 1]):
+            ref[r_] = oracle.swiglu_row(an[r_], w13n[s], w2n[s])
+    mr, l2 = normwise(f64(y), ref)
+    say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
+    assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
+
+
+def test_combine_and_bias_update_match_oracle():
+    require_gpu()
+    rng = np.random.default_rng(21)
+    T, H, k, M = 50, 256, 4, 230
+    wl = workloads.V3_PREFILL.with_(T=T, H=H, N=16, n_groups=1, topk_groups=1, k=k, I=64)
+    cfg = moe.make_cfg(wl)
+    y = synth.normal((M, H), 1.0, torch.bfloat16, "cuda", 2, "y")
+    ysh = synth.normal((T, H), 1.0, torch.bfloat16, "cuda", 2, "ysh")
+    inv = rng.permutation(M)[:T * k].reshape(T, k).astype(np.int32)
+    inv[rng.random((T, k)) < 0.2] = -1
+    gate = rng.random((T, k)).astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(cfg, y, torch.from_numpy(inv).cuda(), torch.from_numpy(gate).cuda(), ysh, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(typed(y), typed(ysh), inv, gate.astype(np.float64))
+    mr, l2 = normwise(f64(out), ref)
+    assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
+    # bias update: exact
+    counts = rng.integers(0, 40, size=16).astype(np.int32)
+    counts[3] = int(round(counts.mean()))
+    bias = rng.uniform(-0.1, 0.1, 16).astype(np.float32)
+    bt = torch.from_numpy(bias.copy()).cuda()
+    moe.moe_bias_update(cfg, torch.from_numpy(counts).cuda(), bt, 0.001)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bt.cpu().numpy(), oracle.bias_update(counts, bias, 0.001))
+
+
+def test_granular_calls_compose_to_layer_forward():
+    """route -> permute -> grouped_ffn -> combine gives the layer's output."""
+    require_gpu()
+    wl = workloads.TINY.with_(T=96, n_shared=0)
+    cfg = moe.make_cfg(wl)
+    inp = make_inputs(wl)
+    out_ref, aux = layer_forward(wl, inp)
+    T, N, k, H = wl.T, wl.N, wl.k, wl.H
+    dev = "cuda"
+    ws = moe.alloc_workspace(cfg)
+    lg = torch.empty((T, N), device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), device=dev)
+    score = torch.empty((T, k), device=dev)
+    moe.moe_route(cfg, inp["x"], inp["w_router"], lg, inp["bias"], idx, gate, score, None, ws)
+    counts = torch.empty(N, dtype=torch.int32, device=dev)
+    offs = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    xp = torch.empty((T * k, H), device=dev)
+    moe.moe_permute(cfg, idx, score, inp["x"], counts, offs, rt, inv, xp, ws=ws)
+    torch.cuda.synchronize()
+    M = int(offs[-1])
+    assert torch.equal(xp[:M], inp["x"][rt[:M].long()])
+    y = torch.empty((T * k, H), device=dev)
+    ws2 = torch.empty(moe.moe_grouped_ffn_workspace_size(cfg, T * k, wl.I), dtype=torch.uint8,
+                      device=dev)
+    moe.moe_grouped_ffn(cfg, N, offs, T * k, wl.I, xp, None, inp["w13"], inp["w2"], y, ws2)
+    out = torch.empty((T, H), device=dev)
+    moe.moe_combine(cfg, y, inv, gate, None, out)
+    torch.cuda.synchronize()
+    mr, _ = normwise(f64(out), f64(out_ref))
+    assert mr <= F32_MAXREL

@@ -170,3 +170,22 @@ def test_bias_update_reduces_imbalance_on_a_fixed_batch():
         ratios.append(c.max() / c.mean())
         b = oracle.bias_update(c.astype(np.int32), b, 0.01)
     assert ratios[-1] < 0.5 * ratios[0]
+
+
+def test_combine_matches_numpy_gather_sum():
+    rng = np.random.default_rng(14)
+    T, H, k, M = 9, 12, 3, 30
+    y = rng.standard_normal((M, H)).astype(np.float32)
+    ysh = rng.standard_normal((T, H)).astype(np.float32)
+    inv = rng.permutation(M)[:T * k].reshape(T, k).astype(np.int32)
+    inv[2, 1] = -1
+    inv[5, :] = -1
+    g = rng.random((T, k))
+    out = oracle.combine(y, ysh, inv, g)
+    ref = ysh.astype(np.float64).copy()
+    for t in range(T):
+        for j in range(k):
+            if inv[t, j] >= 0:
+                ref[t] += g[t, j] * y[inv[t, j]].astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.combine(y, None, inv, g), ref - ysh, rtol=1e-12, atol=1e-12)
