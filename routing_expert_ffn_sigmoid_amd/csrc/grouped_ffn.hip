@@ -26,6 +26,28 @@
 
 namespace moe {
 
+// Tile configuration of the three tile families (rows per tile = 16 * MB,
+// weight fragments prefetched PF steps ahead); overridable at build time.
+#ifndef MOE_FFN_BIG_MB
+#define MOE_FFN_BIG_MB 8
+#endif
+#ifndef MOE_FFN_BIG_PF
+#define MOE_FFN_BIG_PF 1
+#endif
+#ifndef MOE_FFN_MID_MB
+#define MOE_FFN_MID_MB 4
+#endif
+#ifndef MOE_FFN_MID_PF
+#define MOE_FFN_MID_PF 2
+#endif
+#ifndef MOE_FFN_SMALL_PF
+#define MOE_FFN_SMALL_PF 4
+#endif
+
+#ifndef MOE_FFN_MINBLK
+#define MOE_FFN_MINBLK 2
+#endif
+
 constexpr int kBK = 64;        // k per pipeline step (8 chunks of 16 bytes)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kMaxSegs = 1024; // flat segments over all groups per launch
@@ -44,6 +66,17 @@ __device__ __forceinline__ int seg_end(const FfnGroup& g, int s) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Threads beyond the first 256 of a larger workgroup pass the same barriers
+// as build_tile_starts without work.
+__device__ __forceinline__ void build_tile_starts_idle() {
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    __syncthreads();
+    __syncthreads();
+  }
+  __syncthreads();
+}
 
 // Exclusive prefix of `cnt` tiles per flat segment into tstart[0..n].
 template <int BM>
@@ -84,18 +117,194 @@ __device__ void build_tile_starts(const FfnLaunch& a, int nsegT, int* tstart, in
   __syncthreads();
 }
 
-template <int MB, int PF, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void ffn_bf16_kernel(FfnLaunch a) {
-  constexpr int BM = 16 * MB;
-  constexpr int APASS = (BM * 8 + kThreads - 1) / kThreads;  // 16-byte A loads per thread
-  constexpr int NSLOT = PF + 1;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * kBK];
-  __shared__ int tstart[kMaxSegs + 1];
-  __shared__ int tmp[kThreads];
+// Rows/columns a tile works on, decoded once per tile.
+struct TileCtx {
+  FfnGroup g;  // a copy: uniform values, no pointer into the kernel arguments
+  int s;       // segment
+  int nt;      // n-tile
+  int mrow0;   // first problem row of the tile
+  int mv;      // valid rows in the tile (1..BM)
+};
 
+// One tile with NMB live M-blocks of 16 rows (NMB*16 >= mv), all loops
+// static.  MFMA operands are (weights, activations), so the accumulator of
+// a lane holds 4 consecutive output columns of one row: D'[4*(lane/16)+i]
+// [lane%16] = out[row lane%16][col 4*(lane/16)+i].
+template <int NMB, int PF, bool SWIGLU>
+__device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__ As) {
+  constexpr int ROWS = 16 * NMB;
+  constexpr int APASS = (ROWS * 8 + kThreads - 1) / kThreads;
+  constexpr int NSLOT = PF + 1;
+  constexpr int BUF = ROWS * kBK;  // elements per LDS buffer
+  const FfnGroup& g = c.g;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int K = g.K;
+  const int nk = K / kBK;
+
+  // activation loader: thread -> (row, 16-byte chunk); rows past the valid
+  // ones reload the last valid row (never read back into a stored output)
+  const bf16_t* A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* aptr[APASS];
+  int aoff[APASS];
+  bool aact[APASS];
+#pragma unroll
+  for (int p = 0; p < APASS; ++p) {
+    const int row = (tid >> 3) + 32 * p;
+    const int ch = tid & 7;
+    aact[p] = row < ROWS;
+    int prow = c.mrow0 + min(row, c.mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aptr[p] = A + static_cast<int64_t>(prow) * g.lda + ch * 8;
+    const int r = aact[p] ? row : 0;
+    aoff[p] = r * kBK + ((ch ^ ((r >> 1) & 7)) * 8);
+  }
+
+  // weight rows of this wave: 4 blocks of 16
+  const bf16_t* W = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(c.s) * g.w_stride;
+  const bf16_t* bptr[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    int brow;
+    if (SWIGLU) {
+      const int col = c.nt * 128 + wave * 32 + (nb & 1) * 16 + (lane & 15);
+      const int cc = col < g.n_out ? col : 0;
+      brow = (nb < 2) ? cc : g.up_off + cc;
+    } else {
+      const int col = c.nt * 256 + wave * 64 + nb * 16 + (lane & 15);
+      brow = col < g.n_out ? col : 0;
+    }
+    bptr[nb] = W + static_cast<int64_t>(brow) * K + (lane >> 4) * 8;
+  }
+
+  f32x4 acc[NMB][4];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 bbuf[NSLOT][2][4];
+  u32x4 areg[APASS];
+
+  auto load_b = [&](int step, u32x4 (&dst)[2][4]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        dst[ks][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + step * kBK + ks * 32);
+  };
+  auto load_a = [&](int step) {
+#pragma unroll
+    for (int p = 0; p < APASS; ++p)
+      if (aact[p]) areg[p] = *reinterpret_cast<const u32x4*>(aptr[p] + step * kBK);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < APASS; ++p)
+      if (aact[p]) *reinterpret_cast<u32x4*>(As + buf * BUF + aoff[p]) = areg[p];
+  };
+  auto compute = [&](int buf, const u32x4 (&b)[2][4]) {
+    const bf16_t* Ab = As + buf * BUF;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int row = mb * 16 + (lane & 15);
+        const int ch = ks * 4 + (lane >> 4);
+        const bf16x8 af = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(Ab + row * kBK + ((ch ^ ((row >> 1) & 7)) * 8)));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b[ks][nb]), af,
+                                                                acc[mb][nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < nk) load_b(u, bbuf[u]);
+  load_a(0);
+  store_a(0);
+  __syncthreads();
+
+  // main loop, unrolled by NSLOT so the register ring is indexed statically
+  for (int s0 = 0; s0 < nk; s0 += NSLOT) {
+#pragma unroll
+    for (int u = 0; u < NSLOT; ++u) {
+      const int st = s0 + u;
+      if (st < nk) {
+        if (st + PF < nk) load_b(st + PF, bbuf[(u + PF) % NSLOT]);
+        if (st + 1 < nk) load_a(st + 1);
+        compute(st & 1, bbuf[u]);
+        if (st + 1 < nk) store_a((st + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: 4 consecutive columns of one row per lane -> one 8-byte store
+  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+  const int rl = lane & 15;
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int r = mb * 16 + rl;
+    if (r < c.mv) {
+      bf16_t* orow = Out + static_cast<int64_t>(c.mrow0 + r) * g.ldo;
+      if (SWIGLU) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = c.nt * 128 + wave * 32 + nb * 16 + cq;
+          if (col < g.n_out) {
+            uint32_t w[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float g0 = acc[mb][nb][2 * h], g1 = acc[mb][nb][2 * h + 1];
+              const float u0 = acc[mb][nb + 2][2 * h], u1 = acc[mb][nb + 2][2 * h + 1];
+              const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+              const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+              w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+            }
+            *reinterpret_cast<u32x2*>(orow + col) = u32x2{w[0], w[1]};
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = c.nt * 256 + wave * 64 + nb * 16 + cq;
+          if (col < g.n_out) {
+            const uint32_t w0 = f32_to_bf16(acc[mb][nb][0]) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[mb][nb][1])) << 16);
+            const uint32_t w1 = f32_to_bf16(acc[mb][nb][2]) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[mb][nb][3])) << 16);
+            *reinterpret_cast<u32x2*>(orow + col) = u32x2{w0, w1};
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int NMB, int PF, bool SWIGLU>
+__device__ __forceinline__ void run_tile(const TileCtx& c, int nmb, bf16_t* As) {
+  if constexpr (NMB == 1) {
+    gemm_tile<1, PF, SWIGLU>(c, As);
+  } else {
+    if (nmb > NMB / 2) gemm_tile<NMB, PF, SWIGLU>(c, As);
+    else run_tile<NMB / 2, PF, SWIGLU>(c, nmb, As);
+  }
+}
+
+template <int MB, int PF, bool SWIGLU>
+__global__ __launch_bounds__(kThreads, MOE_FFN_MINBLK) void ffn_bf16_kernel(FfnLaunch a) {
+  constexpr int BM = 16 * MB;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2 * BM * kBK];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
   build_tile_starts<BM>(a, nsegT, tstart, tmp);
   const int total = tstart[nsegT];
@@ -108,7 +317,6 @@ __global__ __launch_bounds__(kThreads) void ffn_bf16_kernel(FfnLaunch a) {
   const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
 
   for (int L = lo + slot; L < hi; L += per) {
-    // ---- decode the tile
     int i0 = 0, i1 = nsegT;
     while (i1 - i0 > 1) {
       const int mid = (i0 + i1) >> 1;
@@ -116,148 +324,138 @@ __global__ __launch_bounds__(kThreads) void ffn_bf16_kernel(FfnLaunch a) {
       else i1 = mid;
     }
     const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
-    const FfnGroup& g = grp ? a.g[1] : a.g[0];
-    const int s = grp ? i0 - a.g[0].nseg : i0;
-    const int r0 = seg_begin(g, s);
-    const int rows = seg_end(g, s) - r0;
+    TileCtx c;
+    c.g = grp ? a.g[1] : a.g[0];
+    c.s = grp ? i0 - a.g[0].nseg : i0;
+    const int r0 = seg_begin(c.g, c.s);
+    const int rows = seg_end(c.g, c.s) - r0;
     const int mtc = (rows + BM - 1) / BM;
     const int local = L - tstart[i0];
-    const int nt = local / mtc;
-    const int mt = local - nt * mtc;
-    const int mrow0 = r0 + mt * BM;
-    const int mv = min(BM, rows - mt * BM);
-    const int nmb = (mv + 15) >> 4;
-    const int K = g.K;
-    const int nk = K / kBK;
-
-    // ---- activation loader: thread -> (row, 16-byte chunk)
-    const bf16_t* A = static_cast<const bf16_t*>(g.A);
-    const bf16_t* aptr[APASS];
-    bool aval[APASS];
-    int aoff[APASS];
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int row = (tid >> 3) + 32 * p;
-      const int ch = tid & 7;
-      aval[p] = (row < BM) && (row < mv);
-      int prow = mrow0 + (row < mv ? row : 0);
-      if (g.row_index) prow = g.row_index[prow];
-      aptr[p] = A + static_cast<int64_t>(prow) * g.lda + ch * 8;
-      aoff[p] = (row < BM ? row : 0) * kBK + ((ch ^ ((row >> 1) & 7)) * 8);
-    }
-
-    // ---- weight rows of this wave (4 blocks of 16)
-    const bf16_t* W = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride;
-    const bf16_t* bptr[4];
-    int col[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      int c, brow;
-      if (SWIGLU) {
-        c = nt * 128 + wave * 32 + (nb & 1) * 16 + (lane & 15);
-        const int cc = c < g.n_out ? c : 0;
-        brow = (nb < 2) ? cc : g.up_off + cc;
-      } else {
-        c = nt * 256 + wave * 64 + nb * 16 + (lane & 15);
-        brow = c < g.n_out ? c : 0;
-      }
-      col[nb] = c;
-      bptr[nb] = W + static_cast<int64_t>(brow) * K + (lane >> 4) * 8;
-    }
-
-    f32x4 acc[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 bbuf[NSLOT][2][4];
-    u32x4 areg[APASS];
-
-    auto load_b = [&](int step, u32x4 (&dst)[2][4]) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          dst[ks][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + step * kBK + ks * 32);
-    };
-    auto load_a = [&](int step) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p)
-        if (aval[p]) areg[p] = *reinterpret_cast<const u32x4*>(aptr[p] + step * kBK);
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-      for (int p = 0; p < APASS; ++p)
-        if (aval[p]) *reinterpret_cast<u32x4*>(&As[buf][aoff[p]]) = areg[p];
-    };
-    auto compute = [&](int buf, const u32x4 (&b)[2][4]) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (mb < nmb) {
-            const int row = mb * 16 + (lane & 15);
-            const int ch = ks * 4 + (lane >> 4);
-            const u32x4 av =
-                *reinterpret_cast<const u32x4*>(&As[buf][row * kBK + ((ch ^ ((row >> 1) & 7)) * 8)]);
-            const bf16x8 af = as_bf16x8(av);
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_bf16x8(b[ks][nb]),
-                                                                    acc[mb][nb], 0, 0, 0);
-          }
-        }
-      }
-    };
-
-    // ---- prologue
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-      if (u < nk) load_b(u, bbuf[u]);
-    load_a(0);
-    store_a(0);
+    c.nt = local / mtc;
+    const int mt = local - c.nt * mtc;
+    c.mrow0 = r0 + mt * BM;
+    c.mv = min(BM, rows - mt * BM);
+    const int nmb = (c.mv + 15) >> 4;
+    // the smallest compiled tile height (MB, MB/2, ..., 1 blocks) covering
+    // the valid rows
+    run_tile<MB, PF, SWIGLU>(c, nmb, As);
     __syncthreads();
+  }
+}
 
-    // ---- main loop, unrolled by NSLOT so the register ring is static
-    for (int s0 = 0; s0 < nk; s0 += NSLOT) {
+// =====================================================================
+// Large-segment kernel (prefill-sized segments, >= ~128 rows per expert).
+//
+// One workgroup per CU computes a 256-row x 256-weight-row tile with 4 waves
+// in a 2x2 layout.  Both operands stream global -> LDS with gfx950's direct
+// loads (global_load_lds_dwordx4), double buffered, so no registers stage
+// them; each wave then reads 16-byte MFMA fragments from LDS.  A wave owns
+// the 8 M-blocks of one parity (blocks 2j + wm), so a tile with fewer rows
+// shortens every wave's work equally.  Row splits of a segment are balanced
+// (ceil(rows / tiles) rows each), so the tiles that share an expert's
+// weights cost the same and stream them through L2 together.
+// =====================================================================
+constexpr int kBigRows = 256;   // max rows per tile
+constexpr int kBigCols = 256;   // weight rows per tile
+constexpr int kBigBufElems = 256 * kBK;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor: no
+// swizzle, 32-bit data); loads past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// One wave moves 8 rows x 128 bytes of an operand tile straight into LDS:
+// lane -> 16 bytes at lds_group + 16 * lane (row lane/8, physical chunk
+// lane%8).  voffset already selects the logical chunk the XOR swizzle keeps
+// at that physical position.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                      bf16_t* lds_group) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_group, 16, voffset, soffset, 0, 0);
+}
+
+constexpr int kBigThreads = 512;  // 8 waves, 2 per SIMD
+
+// Wave (wm, wn) = (wave & 1, wave >> 1): M-blocks 2j + wm (j < NMBW), four
+// 16-row weight blocks; gate/up phase: gate blocks 2wn, 2wn+1 and the up
+// blocks 8 + 2wn, 8 + 2wn + 1 (same h columns), plain phase: 4wn .. 4wn+3.
+template <bool SWIGLU>
+__device__ __forceinline__ int big_wblock(int wn, int nb) {
+  if (SWIGLU) return (nb < 2 ? 0 : 8) + wn * 2 + (nb & 1);
+  return wn * 4 + nb;
+}
+
+template <int NMBW, bool SWIGLU>
+__device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
+                                            const bf16_t* __restrict__ Bb, f32x4 (&acc)[8][4],
+                                            int wm, int wn) {
+  const int lane = threadIdx.x & 63;
+  // every fragment row is 16*block + lane%16, so the swizzle term
+  // ((row >> 1) & 7) is (lane%16) >> 1 for all blocks: one base address per
+  // operand, block offsets are immediates
+  const int swz = (lane & 15) >> 1;
 #pragma unroll
-      for (int u = 0; u < NSLOT; ++u) {
-        const int st = s0 + u;
-        if (st < nk) {
-          if (st + PF < nk) load_b(st + PF, bbuf[(u + PF) % NSLOT]);
-          if (st + 1 < nk) load_a(st + 1);
-          compute(st & 1, bbuf[u]);
-          if (st + 1 < nk) store_a((st + 1) & 1);
-          __syncthreads();
-        }
-      }
+  for (int ks = 0; ks < 2; ++ks) {
+    const int ch = (ks * 4 + (lane >> 4)) ^ swz;
+    const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK + ch * 8;
+    const bf16_t* bbase = Bb + (lane & 15) * kBK + ch * 8;
+    bf16x8 bf[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK));
+#pragma unroll
+    for (int j = 0; j < NMBW; ++j) {
+      const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af, acc[j][nb], 0, 0, 0);
     }
+  }
+}
 
-    // ---- epilogue: D element i of a lane is row 4*(lane/16)+i, col lane%16
-    bf16_t* Out = static_cast<bf16_t*>(g.Out);
+template <bool SWIGLU>
+__device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&acc)[8][4],
+                                             int nmbw, int wm, int wn, int nt, int mrow0,
+                                             int mv) {
+  const int lane = threadIdx.x & 63;
+  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+  const int rl = lane & 15;
+  const int cq = (lane >> 4) * 4;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb < nmb) {
+  for (int j = 0; j < 8; ++j) {
+    if (j < nmbw) {
+      const int r = (2 * j + wm) * 16 + rl;
+      if (r < mv) {
+        bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
+        if (SWIGLU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mb * 16 + (lane >> 4) * 4 + i;
-          if (r < mv) {
-            bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
-            if (SWIGLU) {
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = nt * 128 + wn * 32 + nb * 16 + cq;
+            if (col < g.n_out) {
+              uint32_t w[2];
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb) {
-                if (col[nb] < g.n_out) {
-                  const float gv = acc[mb][nb][i];
-                  const float uv = acc[mb][nb + 2][i];
-                  const float h = gv / (1.0f + __expf(-gv)) * uv;
-                  orow[col[nb]] = f32_to_bf16(h);
-                }
+              for (int h = 0; h < 2; ++h) {
+                const float g0 = acc[j][nb][2 * h], g1 = acc[j][nb][2 * h + 1];
+                const float u0 = acc[j][nb + 2][2 * h], u1 = acc[j][nb + 2][2 * h + 1];
+                const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+                const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+                w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
               }
-            } else {
+              *reinterpret_cast<u32x2*>(orow + col) = u32x2{w[0], w[1]};
+            }
+          }
+        } else {
 #pragma unroll
-              for (int nb = 0; nb < 4; ++nb)
-                if (col[nb] < g.n_out) orow[col[nb]] = f32_to_bf16(acc[mb][nb][i]);
+          for (int nb = 0; nb < 4; ++nb) {
+            const int col = nt * 256 + wn * 64 + nb * 16 + cq;
+            if (col < g.n_out) {
+              const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
+                                  (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
+              const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
+                                  (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
+              *reinterpret_cast<u32x2*>(orow + col) = u32x2{w0, w1};
             }
           }
         }
@@ -265,6 +463,138 @@ __global__ __launch_bounds__(kThreads) void ffn_bf16_kernel(FfnLaunch a) {
     }
   }
 }
+
+// The k-loop of one tile with NMBW live M-blocks per wave.
+template <int NMBW, bool SWIGLU>
+__device__ __noinline__ void big_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                         bf16_t* As0, bf16_t* As1, bf16_t* Bs0, bf16_t* Bs1) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int K = g.K;
+  const int nk = K / kBK;
+
+  // 4 DMA row groups per operand per thread: group q = p*8 + wave covers
+  // tile rows [8q, 8q+8); this lane brings row 8q + lane/8, physical chunk
+  // lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7), where
+  // (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.
+  const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
+  uint32_t aoff[4];
+  const int rows_needed = (2 * NMBW) * 16;  // tile rows any wave reads
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = (p * 8 + wave) * 8 + (lane >> 3);
+    int prow = mrow0 + min(row, mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+  }
+  // weight rows: tile row r = p*64 + 8*wave + lane/8
+  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
+  const int col0 = SWIGLU ? nt * 128 : nt * 256;
+  const uint32_t boff =
+      static_cast<uint32_t>(col0 + wave * 8 + (lane >> 3)) * krow_bytes + logical * 16;
+  auto b_soff = [&](int p) -> uint32_t {
+    // tile rows p*64..; in the gate/up phase rows 128.. are the up half
+    if (SWIGLU && p >= 2) return static_cast<uint32_t>(g.up_off + (p - 2) * 64) * krow_bytes;
+    return static_cast<uint32_t>(p * 64) * krow_bytes;
+  };
+
+  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
+    const uint32_t kb = static_cast<uint32_t>(step) * (kBK * 2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int q = p * 8 + wave;
+      if (q * 8 < rows_needed) dma16(ra, aoff[p], kb, Ab + q * 8 * kBK);
+      dma16(rb, boff, b_soff(p) + kb, Bb + q * 8 * kBK);
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, As0, Bs0);
+  __syncthreads();
+  // two steps per iteration (buffer 0 then 1); no accumulator update sits
+  // under a condition inside the loop
+  int st = 0;
+  for (; st + 1 < nk; st += 2) {
+    issue(st + 1, As1, Bs1);
+    big_compute<NMBW, SWIGLU>(As0, Bs0, acc, wm, wn);
+    __syncthreads();
+    if (st + 2 < nk) issue(st + 2, As0, Bs0);
+    big_compute<NMBW, SWIGLU>(As1, Bs1, acc, wm, wn);
+    __syncthreads();
+  }
+  if (st < nk) {  // odd step count: the last step sits in buffer 0
+    big_compute<NMBW, SWIGLU>(As0, Bs0, acc, wm, wn);
+    __syncthreads();
+  }
+  big_epilogue<SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
+  __shared__ __attribute__((aligned(16))) bf16_t As0[kBigBufElems];
+  __shared__ __attribute__((aligned(16))) bf16_t As1[kBigBufElems];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs0[kBigBufElems];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs1[kBigBufElems];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
+  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
+  if (threadIdx.x < kThreads) build_tile_starts<kBigRows>(a, nsegT, tstart, tmp);
+  else build_tile_starts_idle();
+  const int total = tstart[nsegT];
+  const int nxcd = 8;
+  const int per = gridDim.x / nxcd;
+  const int xcd = blockIdx.x % nxcd;
+  const int slot = blockIdx.x / nxcd;
+  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
+  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
+
+  for (int L = lo + slot; L < hi; L += per) {
+    int i0 = 0, i1 = nsegT;
+    while (i1 - i0 > 1) {
+      const int mid = (i0 + i1) >> 1;
+      if (tstart[mid] <= L) i0 = mid;
+      else i1 = mid;
+    }
+    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+    const FfnGroup g = grp ? a.g[1] : a.g[0];
+    const int s = grp ? i0 - a.g[0].nseg : i0;
+    const int r0 = seg_begin(g, s);
+    const int rows = seg_end(g, s) - r0;
+    const int mtc = (rows + kBigRows - 1) / kBigRows;
+    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
+    const int local = L - tstart[i0];
+    const int nt = local / mtc;
+    const int mt = local - nt * mtc;
+    const int mrow0 = r0 + mt * rpt;
+    const int mv = min(rpt, rows - mt * rpt);
+    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;  // blocks per wave (interleaved)
+    switch (nmbw) {
+      case 8: big_tile<8, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 7: big_tile<7, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 6: big_tile<6, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 5: big_tile<5, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 4: big_tile<4, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 3: big_tile<3, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      case 2: big_tile<2, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+      default: big_tile<1, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+    }
+    __syncthreads();
+  }
+}
+
+static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st);
 
 static int device_cus() {
   static int cus[64] = {0};
@@ -302,6 +632,23 @@ static hipError_t launch_mb(const FfnLaunch& fl, int phase, int blocks_per_cu, h
   return hipGetLastError();
 }
 
+static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
+  long long ub = 0;
+  for (int i = 0; i < fl.ngroups; ++i)
+    ub += ((static_cast<long long>(fl.g[i].rows) + kBigRows - 1) / kBigRows + fl.g[i].nseg) *
+          static_cast<long long>(fl.nt[i]);
+  if (ub <= 0) return hipSuccess;
+  long long grid = device_cus();
+  const long long ub8 = (ub + 7) / 8 * 8;
+  if (grid > ub8) grid = ub8;
+  grid = (grid + 7) / 8 * 8;
+  if (phase == 0)
+    ffn_big_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+  else
+    ffn_big_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int rows_hint,
                            hipStream_t st) {
   FfnLaunch fl{};
@@ -311,9 +658,15 @@ hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int r
     const int cols = phase == 0 ? 128 : 256;
     fl.nt[i] = (groups[i].n_out + cols - 1) / cols;
   }
-  if (rows_hint >= 128) return launch_mb<8, 1>(fl, phase, 1, st);
-  if (rows_hint >= 32) return launch_mb<4, 2>(fl, phase, 2, st);
-  return launch_mb<1, 4>(fl, phase, 2, st);
+#ifndef MOE_FFN_NO_BIG
+  bool big_ok = true;  // buffer addressing needs 32-bit byte offsets
+  for (int i = 0; i < ngroups; ++i)
+    big_ok = big_ok && groups[i].a_bytes != 0 && groups[i].w_bytes != 0;
+  if (rows_hint >= 128 && big_ok) return launch_big(fl, phase, st);
+#endif
+  if (rows_hint >= 128) return launch_mb<MOE_FFN_BIG_MB, MOE_FFN_BIG_PF>(fl, phase, MOE_FFN_MINBLK, st);
+  if (rows_hint >= 32) return launch_mb<MOE_FFN_MID_MB, MOE_FFN_MID_PF>(fl, phase, 2, st);
+  return launch_mb<1, MOE_FFN_SMALL_PF>(fl, phase, 2, st);
 }
 
 // ================================================================ fp32 path

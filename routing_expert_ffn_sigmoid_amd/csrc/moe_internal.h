@@ -157,6 +157,8 @@ struct FfnGroup {
   int32_t K;                // reduction length
   int32_t n_out;            // output columns (h cols in the gate/up phase)
   int32_t up_off;           // gate/up phase: row offset of the up half (= inter)
+  uint32_t a_bytes;         // bytes addressable from A (buffer bound; 0 = unknown)
+  uint32_t w_bytes;         // bytes of one segment's weights (buffer bound; 0 = unknown)
 };
 // phase 0: gate/up + SwiGLU -> h;  phase 1: down projection -> y.
 // `rows_hint`: expected rows per segment (chooses the tile height).

@@ -173,7 +173,7 @@ def test_bf16_small_layer_parity_and_determinism():
         assert torch.equal(aux[n], aux2[n]), n
 
 
-@pytest.mark.parametrize("rows_per_seg", [5, 40, 150])
+@pytest.mark.parametrize("rows_per_seg", [5, 40, 150, 400])
 def test_grouped_ffn_ragged_segments(rows_per_seg):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height."""
     require_gpu()
@@ -205,6 +205,24 @@ def test_grouped_ffn_ragged_segments(rows_per_seg):
     mr, l2 = normwise(f64(y), ref)
     say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
     assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
+
+
+@pytest.mark.parametrize("T,I", [(1024, 192), (1500, 128)])
+def test_bf16_layer_with_large_segments(T, I):
+    """Segments of ~hundreds of rows (the large-segment kernel), an odd
+    number of k-steps (I = 192) and a ragged token count."""
+    require_gpu()
+    wl = workloads.V3_PREFILL.with_(T=T, H=256, N=8, k=2, n_groups=2, topk_groups=1, I=I,
+                                    I_shared=128)
+    say(f"bf16 large segments T={T} I={I}")
+    inp = make_inputs(wl)
+    out, aux = layer_forward(wl, inp)
+    r = check_routing(wl, aux, inp["bias"])
+    d = check_dispatch(wl, aux, r)
+    toks = list(range(0, wl.T, 37))
+    ref = oracle_rows(wl, inp, r, d, toks)
+    mr, l2 = check_outputs(wl, out, ref, toks)
+    say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
 
 
 def test_combine_and_bias_update_match_oracle():
