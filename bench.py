@@ -160,6 +160,101 @@ def cpu_baseline(wl, inp, logits_gpu, sample: int) -> dict:
                       f"the layer output of each, single-threaded C, {dt:.1f} s"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE readings calibrate the same counters for the
+    library's kernels (bytes the counters report per byte really moved)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": COPY_BYTES}))
+
+
+def _csv_rows(path_glob):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(path_glob, recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_profile(d: str, workload: str, commands: dict):
+    """Turn the raw rocprofv3 output under d (trace/, fetch/, write/,
+    copy_fetch/, copy_write/) into profiles/<kernel>_<workload>.txt and the
+    gate/up traffic record profiles/ffn_gate_up_traffic_<workload>.json."""
+    stats = _csv_rows(os.path.join(d, "trace", "**", "*kernel_stats.csv"))
+    lines = [f"# rocprofv3 summary: DeepSeekMoE layer forward, workload {workload}", ""]
+    for key in ("trace", "fetch", "write", "copy_fetch", "copy_write"):
+        if key in commands:
+            lines.append(f"{key}: {commands[key]}")
+    lines += ["", "## kernel trace (--kernel-trace --stats), library kernels",
+              f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    avg = {}
+    for r in stats:
+        name = r["Name"]
+        if "moe::" not in name:
+            continue
+        short = name.replace("void ", "").split("(")[0]
+        avg[short] = float(r["AverageNs"]) / 1e3
+        lines.append(f"{short:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.1f} "
+                     f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f}")
+
+    def per_kernel(sub, counter):
+        acc = {}
+        for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"].replace("void ", "").split("(")[0]
+            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel("fetch", "FETCH_SIZE")
+    write = per_kernel("write", "WRITE_SIZE")
+    cf = per_kernel("copy_fetch", "FETCH_SIZE")
+    cw = per_kernel("copy_write", "WRITE_SIZE")
+    copy_f = max(cf.values()) if cf else None
+    copy_w = max(cw.values()) if cw else None
+    f_scale = COPY_BYTES / (copy_f * 1024) if copy_f else None
+    w_scale = COPY_BYTES / (copy_w * 1024) if copy_w else None
+    lines += ["", "## HBM traffic per dispatch (FETCH_SIZE / WRITE_SIZE, KiB as read, then "
+              "scaled by a 1 GiB plain copy's readings)",
+              f"copy calibration: FETCH_SIZE {copy_f} KiB, WRITE_SIZE {copy_w} KiB for "
+              f"{COPY_BYTES} B each way -> fetch scale {f_scale}, write scale {w_scale}",
+              f"{'kernel':60s} {'fetch_KiB':>14s} {'write_KiB':>12s} {'bytes(scaled)':>16s}"]
+    traffic = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "moe::" not in k:
+            continue
+        fb = fetch.get(k, 0.0) * 1024 * (f_scale or 1.0)
+        wb = write.get(k, 0.0) * 1024 * (w_scale or 1.0)
+        traffic[k] = fb + wb
+        lines.append(f"{k:60s} {fetch.get(k, 0.0):14.1f} {write.get(k, 0.0):12.1f} {fb + wb:16.4g}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
+    with open(txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    gate_up = [k for k in traffic if "true>" in k and "ffn" in k]
+    if gate_up:
+        k = max(gate_up, key=lambda n: avg.get(n, 0.0))
+        src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")
+        rec = {"kernel": k, "workload": workload, "bytes_per_launch": traffic[k],
+               "fetch_kib": fetch.get(k), "write_kib": write.get(k),
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "avg_launch_us": avg.get(k), "source_digest": source_digest([src]),
+               "commands": commands}
+        with open(os.path.join(ROOT, "profiles", f"ffn_gate_up_traffic_{workload}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,7 +263,25 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarize rocprofv3 output under DIR into profiles/ and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.summarize_profile:
+        cmd = "rocprofv3 {opt} -d <dir> -o run --output-format csv -- python3 bench.py {args}"
+        run = f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline"
+        pmc = f"--workload {args.workload} --steps 2 --warmup 1 --no-cpu-baseline"
+        commands = {"trace": cmd.format(opt="--kernel-trace --stats", args=run),
+                    "fetch": cmd.format(opt="--pmc FETCH_SIZE", args=pmc),
+                    "write": cmd.format(opt="--pmc WRITE_SIZE", args=pmc),
+                    "copy_fetch": cmd.format(opt="--pmc FETCH_SIZE", args="--calibrate-copy"),
+                    "copy_write": cmd.format(opt="--pmc WRITE_SIZE", args="--calibrate-copy")}
+        summarize_profile(args.summarize_profile, args.workload, commands)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
               f"(requested --gpus {args.gpus}); multi-GPU sharding is not implemented.",
