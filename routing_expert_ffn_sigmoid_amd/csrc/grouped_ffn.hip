@@ -361,10 +361,27 @@ constexpr int kBigBufElems = 256 * kBK;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Values every lane of a wave holds equally, made visible to the compiler as
+// such (scalar registers): buffer descriptors and the LDS target of a direct
+// load must be wave-uniform, otherwise the compiler wraps the load in a
+// per-lane loop.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = wave_uniform(static_cast<uint32_t>(v));
+  const uint32_t hi = wave_uniform(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor: no
 // swizzle, 32-bit data); loads past `bytes` return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform(base)), 0,
+                                           wave_uniform(bytes), 0x00020000);
 }
 
 // One wave moves 8 rows x 128 bytes of an operand tile straight into LDS:
@@ -373,7 +390,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // at that physical position.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
                                       bf16_t* lds_group) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_group, 16, voffset, soffset, 0, 0);
+  // lds_group is derived from the wave index made uniform by the caller
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_group, 16, voffset,
+                                           wave_uniform(soffset), 0, 0);
 }
 
 constexpr int kBigThreads = 512;  // 8 waves, 2 per SIMD
@@ -470,10 +489,10 @@ __device__ __noinline__ void big_tile(const FfnGroup& g, int s, int nt, int mrow
                                          bf16_t* As0, bf16_t* As1, bf16_t* Bs0, bf16_t* Bs1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_uniform(tid >> 6);
   const int wm = wave & 1;
   const int wn = wave >> 1;
-  const int K = g.K;
+  const int K = wave_uniform(g.K);
   const int nk = K / kBK;
 
   // 4 DMA row groups per operand per thread: group q = p*8 + wave covers
@@ -594,6 +613,485 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
   }
 }
 
+// ---------------------------------------------------------------------
+// 4-stage variant (k-steps of 32): three stages of both operands are in
+// flight per CU while the fourth is consumed.  Each wave waits for its own
+// loads of the stage it is about to read (s_waitcnt vmcnt) *before* the
+// workgroup barrier, so after the barrier every wave's share of that stage
+// is in LDS; the barrier also retires the reads of the buffer the next load
+// overwrites.  Used when K is a multiple of 128.
+// ---------------------------------------------------------------------
+constexpr int kBK4 = 32;
+constexpr int kStages = 4;
+constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB per operand stage
+
+// s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 3 stages x 4 + 3
+  }
+}
+
+#ifndef MOE_FFN_L2_PREFETCH
+#define MOE_FFN_L2_PREFETCH 0
+#endif
+
+template <int NMBW, bool SWIGLU>
+__device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
+                                             const bf16_t* __restrict__ Bb, f32x4 (&acc)[8][4],
+                                             int wm, int wn) {
+  const int lane = threadIdx.x & 63;
+  // fragment row = 16*block + lane%16; swizzle term ((row >> 1) & 3) is
+  // ((lane%16) >> 1) & 3: one base per operand, block offsets are immediates
+  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
+  const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
+  const bf16_t* bbase = Bb + (lane & 15) * kBK4 + ch * 8;
+  bf16x8 bf[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK4));
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j) {
+    const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK4));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af, acc[j][nb], 0, 0, 0);
+  }
+}
+
+template <int NMBW, bool SWIGLU>
+__device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                       bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
+                                       bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3,
+                                       bf16_t* scratch) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int K = wave_uniform(g.K);
+  const int nk = K / kBK4;  // multiple of 4
+
+  // DMA geometry: 16 rows x 64 bytes per wave instruction; row group
+  // q = p*8 + wave covers tile rows [16q, 16q+16); lane -> row 16q + lane/4,
+  // physical chunk lane%4, logical chunk (lane%4) ^ ((row >> 1) & 3), and
+  // (row >> 1) & 3 = (lane >> 3) & 3 for every q.  (With 64-byte rows this
+  // XOR of row pairs is the pattern that keeps 16-byte fragment reads free
+  // of bank conflicts on gfx950; XOR by row quads is not.)
+  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
+  const int rows_needed = (2 * NMBW) * 16;
+  uint32_t aoff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = (p * 8 + wave) * 16 + (lane >> 2);
+    int prow = mrow0 + min(row, mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+  }
+  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
+  const int col0 = SWIGLU ? nt * 128 : nt * 256;
+  const uint32_t boff =
+      static_cast<uint32_t>(col0 + wave * 16 + (lane >> 2)) * krow_bytes + logical * 16;
+  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
+  const bool a0 = (0 * 8 + wave) * 16 < rows_needed;
+  const bool a1 = (1 * 8 + wave) * 16 < rows_needed;
+
+  // Every vector-memory instruction this wave issues in the tile is counted
+  // (cnt); mark[b] is cnt right after stage b's loads.  Waiting for stage b
+  // = s_waitcnt vmcnt(cnt - mark[b]): vmcnt retires in issue order.
+  int cnt = 0;
+  int mark[kStages] = {0, 0, 0, 0};
+  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
+    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
+    if (a0) dma16(ra, aoff[0], kb, Ab + (0 * 8 + wave) * 16 * kBK4);
+    if (a1) dma16(ra, aoff[1], kb, Ab + (1 * 8 + wave) * 16 * kBK4);
+    dma16(rb, boff, kb, Bb + (0 * 8 + wave) * 16 * kBK4);
+    dma16(rb, boff, bsoff1 + kb, Bb + (1 * 8 + wave) * 16 * kBK4);
+    cnt += 2 + (a0 ? 1 : 0) + (a1 ? 1 : 0);
+  };
+#if MOE_FFN_L2_PREFETCH > 0
+  // L2 warm-up of stages still further ahead: one 16-byte request per
+  // 128-byte line (two k-steps of 32), one wave instruction per 64 rows;
+  // waves 0-3 cover the 256 activation rows, waves 4-7 the 256 weight rows.
+  // The bytes land in a wave-private scratch slot of LDS and are never read.
+  uint32_t pf_off;
+  {
+    const int r = (wave & 3) * 64 + lane;
+    if (wave < 4) {
+      int prow = mrow0 + min(r, mv - 1);
+      if (g.row_index) prow = g.row_index[prow];
+      pf_off = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u;
+    } else {
+      const int brow = SWIGLU ? (r < 128 ? col0 + r : g.up_off + col0 + (r - 128)) : col0 + r;
+      pf_off = static_cast<uint32_t>(brow) * krow_bytes;
+    }
+  }
+  const bool pf_active = wave < 4 ? ((wave & 3) * 64 < rows_needed) : true;
+  auto prefetch = [&](int step) {  // lines of steps (step, step+1), step even
+    if (step < nk && pf_active) {
+      dma16(wave < 4 ? ra : rb, pf_off, static_cast<uint32_t>(step) * (kBK4 * 2),
+            scratch + wave * 512);
+      ++cnt;
+    }
+  };
+#else
+  auto prefetch = [&](int) {};
+#endif
+  auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, A0, B0);
+  mark[0] = cnt;
+  issue(1, A1, B1);
+  mark[1] = cnt;
+  issue(2, A2, B2);
+  mark[2] = cnt;
+  constexpr int PD = MOE_FFN_L2_PREFETCH;  // stages beyond the loads in flight
+  for (int st = 0; st < nk; st += kStages) {
+    // step st (buffer 0)
+    wait_stage(0);
+    __builtin_amdgcn_s_barrier();
+    if (st + 3 < nk) issue(st + 3, A3, B3);
+    mark[3] = cnt;
+    if (PD > 0) prefetch(st + 3 + PD + ((3 + PD) & 1));
+    big4_compute<NMBW, SWIGLU>(A0, B0, acc, wm, wn);
+    // step st+1 (buffer 1)
+    wait_stage(1);
+    __builtin_amdgcn_s_barrier();
+    if (st + 4 < nk) issue(st + 4, A0, B0);
+    mark[0] = cnt;
+    big4_compute<NMBW, SWIGLU>(A1, B1, acc, wm, wn);
+    // step st+2 (buffer 2)
+    wait_stage(2);
+    __builtin_amdgcn_s_barrier();
+    if (st + 5 < nk) issue(st + 5, A1, B1);
+    mark[1] = cnt;
+    if (PD > 0) prefetch(st + 5 + PD + ((5 + PD) & 1));
+    big4_compute<NMBW, SWIGLU>(A2, B2, acc, wm, wn);
+    // step st+3 (buffer 3)
+    wait_stage(3);
+    __builtin_amdgcn_s_barrier();
+    if (st + 6 < nk) issue(st + 6, A2, B2);
+    mark[2] = cnt;
+    big4_compute<NMBW, SWIGLU>(A3, B3, acc, wm, wn);
+  }
+  big_epilogue<SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
+  __shared__ __attribute__((aligned(16))) bf16_t A0[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t A1[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t A2[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t A3[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t Pf[8 * 512];  // L2 warm-up landing slots
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
+  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
+  if (threadIdx.x < kThreads) build_tile_starts<kBigRows>(a, nsegT, tstart, tmp);
+  else build_tile_starts_idle();
+  const int total = tstart[nsegT];
+  const int nxcd = 8;
+  const int per = gridDim.x / nxcd;
+  const int xcd = blockIdx.x % nxcd;
+  const int slot = blockIdx.x / nxcd;
+  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
+  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
+
+  for (int L = lo + slot; L < hi; L += per) {
+    int i0 = 0, i1 = nsegT;
+    while (i1 - i0 > 1) {
+      const int mid = (i0 + i1) >> 1;
+      if (tstart[mid] <= L) i0 = mid;
+      else i1 = mid;
+    }
+    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+    const FfnGroup g = grp ? a.g[1] : a.g[0];
+    const int s = grp ? i0 - a.g[0].nseg : i0;
+    const int r0 = seg_begin(g, s);
+    const int rows = seg_end(g, s) - r0;
+    const int mtc = (rows + kBigRows - 1) / kBigRows;
+    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
+    const int local = L - tstart[i0];
+    const int nt = local / mtc;
+    const int mt = local - nt * mtc;
+    const int mrow0 = r0 + mt * rpt;
+    const int mv = min(rpt, rows - mt * rpt);
+    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
+    switch (nmbw) {
+      case 8: big4_tile<8, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 7: big4_tile<7, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 6: big4_tile<6, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 5: big4_tile<5, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 4: big4_tile<4, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 3: big4_tile<3, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      case 2: big4_tile<2, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+      default: big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------
+// Weight-streaming variant for large segments.  Only the activation tile is
+// staged in LDS (kAStages stages of 32 k, kAStages-1 in flight); each of the
+// 8 waves owns two 16-row weight blocks of the 256-wide tile (gate/up phase:
+// the gate and the up block of the same 16 h-columns) and streams them from
+// memory straight into registers kBPF steps ahead.  Every wave computes all
+// tile rows, so a short tile shortens every wave's work.
+// ---------------------------------------------------------------------
+#ifndef MOE_FFN_A_STAGES
+#define MOE_FFN_A_STAGES 6
+#endif
+#ifndef MOE_FFN_B_PF
+#define MOE_FFN_B_PF 5
+#endif
+constexpr int kAStages = MOE_FFN_A_STAGES;
+constexpr int kBPF = MOE_FFN_B_PF;
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+template <int NMB, bool SWIGLU>
+__device__ __noinline__ void big5_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                       bf16_t* As) {
+  constexpr int BUF = 256 * kBK4;  // elements per activation stage
+  constexpr int NSLOT = kBPF + 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int K = wave_uniform(g.K);
+  const int nk = K / kBK4;
+
+  // activation DMA: 16 rows x 64 bytes per wave instruction, row group
+  // q = p*8 + wave (p = 0, 1) covers rows [16q, 16q+16); lane -> row
+  // 16q + lane/4, physical chunk lane%4, logical chunk
+  // (lane%4) ^ ((row >> 1) & 3) = (lane%4) ^ ((lane >> 3) & 3)
+  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const int rows_needed = NMB * 16;
+  uint32_t aoff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = (p * 8 + wave) * 16 + (lane >> 2);
+    int prow = mrow0 + min(row, mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+  }
+  const bool a0 = (0 * 8 + wave) * 16 < rows_needed;
+  const bool a1 = (1 * 8 + wave) * 16 < rows_needed;
+
+  // weight fragments of this wave: block nb (0, 1), lane -> row lane%16,
+  // k-chunk lane/16 of each 32-wide step
+  const bf16_t* W = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride;
+  const bf16_t* bptr[2];
+  int col[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    int c, brow;
+    if (SWIGLU) {
+      c = nt * 128 + wave * 16 + (lane & 15);
+      const int cc = c < g.n_out ? c : g.n_out - 1;
+      brow = nb == 0 ? cc : g.up_off + cc;
+    } else {
+      c = nt * 256 + wave * 32 + nb * 16 + (lane & 15);
+      brow = c < g.n_out ? c : g.n_out - 1;
+    }
+    col[nb] = c;
+    bptr[nb] = W + static_cast<int64_t>(brow) * K + (lane >> 4) * 8;
+  }
+
+  int cnt = 0;              // vector-memory instructions issued by this wave
+  int mark[kAStages] = {};  // cnt after each activation stage's loads
+  auto issue_a = [&](int step, int buf) {
+    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
+    bf16_t* Ab = As + buf * BUF;
+    if (a0) dma16(ra, aoff[0], kb, Ab + (0 * 8 + wave) * 16 * kBK4);
+    if (a1) dma16(ra, aoff[1], kb, Ab + (1 * 8 + wave) * 16 * kBK4);
+    cnt += (a0 ? 1 : 0) + (a1 ? 1 : 0);
+  };
+  u32x4 bbuf[NSLOT][2];
+  auto issue_b = [&](int step, u32x4 (&dst)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      dst[nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + step * kBK4);
+    cnt += 2;
+  };
+
+  f32x4 acc[NMB][2];
+#pragma unroll
+  for (int j = 0; j < NMB; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
+  auto compute = [&](int buf, const u32x4 (&b)[2]) {
+    const bf16_t* abase = As + buf * BUF + (lane & 15) * kBK4 + ch * 8;
+    const bf16x8 b0 = as_bf16x8(b[0]);
+    const bf16x8 b1 = as_bf16x8(b[1]);
+#pragma unroll
+    for (int j = 0; j < NMB; ++j) {
+      const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 16 * kBK4));
+      acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, af, acc[j][0], 0, 0, 0);
+      acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, af, acc[j][1], 0, 0, 0);
+    }
+  };
+
+  // prologue: weights for steps 0..kBPF-1, activations for stages 0..S-2
+#pragma unroll
+  for (int u = 0; u < kBPF; ++u)
+    if (u < nk) issue_b(u, bbuf[u]);
+#pragma unroll
+  for (int u = 0; u < kAStages - 1; ++u) {
+    if (u < nk) issue_a(u, u);
+    mark[u] = cnt;
+  }
+  // main loop: the activation buffer index advances mod kAStages and the
+  // weight slot mod NSLOT; both are static inside an unrolled block of
+  // lcm(kAStages, NSLOT) steps
+  constexpr int UNR = kAStages * NSLOT / gcd_c(kAStages, NSLOT);
+  for (int s0 = 0; s0 < nk; s0 += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int st = s0 + u;
+      if (st < nk) {
+        const int abuf = u % kAStages;
+        wait_vmcnt_dyn(cnt - mark[abuf]);
+        __builtin_amdgcn_s_barrier();
+        if (st + kAStages - 1 < nk) issue_a(st + kAStages - 1, (u + kAStages - 1) % kAStages);
+        mark[(u + kAStages - 1) % kAStages] = cnt;
+        if (st + kBPF < nk) issue_b(st + kBPF, bbuf[(u + kBPF) % NSLOT]);
+        compute(abuf, bbuf[u % NSLOT]);
+      }
+    }
+  }
+
+  // epilogue: rows mrow0 + 16j + lane%16, 4 consecutive columns per lane
+  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+  const int rl = lane & 15;
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int j = 0; j < NMB; ++j) {
+    const int r = j * 16 + rl;
+    if (r < mv) {
+      bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
+      if (SWIGLU) {
+        const int cc = nt * 128 + wave * 16 + cq;
+        if (cc < g.n_out) {
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float g0 = acc[j][0][2 * h], g1 = acc[j][0][2 * h + 1];
+            const float u0 = acc[j][1][2 * h], u1 = acc[j][1][2 * h + 1];
+            const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+            const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+            w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+          }
+          *reinterpret_cast<u32x2*>(orow + cc) = u32x2{w[0], w[1]};
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int cc = nt * 256 + wave * 32 + nb * 16 + cq;
+          if (cc < g.n_out) {
+            const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
+            const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
+            *reinterpret_cast<u32x2*>(orow + cc) = u32x2{w0, w1};
+          }
+        }
+      }
+    }
+  }
+  (void)col;
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_big5_kernel(FfnLaunch a) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[kAStages * 256 * kBK4];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
+  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
+  if (threadIdx.x < kThreads) build_tile_starts<kBigRows>(a, nsegT, tstart, tmp);
+  else build_tile_starts_idle();
+  const int total = tstart[nsegT];
+  const int nxcd = 8;
+  const int per = gridDim.x / nxcd;
+  const int xcd = blockIdx.x % nxcd;
+  const int slot = blockIdx.x / nxcd;
+  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
+  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
+
+  for (int L = lo + slot; L < hi; L += per) {
+    int i0 = 0, i1 = nsegT;
+    while (i1 - i0 > 1) {
+      const int mid = (i0 + i1) >> 1;
+      if (tstart[mid] <= L) i0 = mid;
+      else i1 = mid;
+    }
+    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+    const FfnGroup g = grp ? a.g[1] : a.g[0];
+    const int s = grp ? i0 - a.g[0].nseg : i0;
+    const int r0 = seg_begin(g, s);
+    const int rows = seg_end(g, s) - r0;
+    const int mtc = (rows + kBigRows - 1) / kBigRows;
+    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
+    const int local = L - tstart[i0];
+    const int nt = local / mtc;
+    const int mt = local - nt * mtc;
+    const int mrow0 = r0 + mt * rpt;
+    const int mv = min(rpt, rows - mt * rpt);
+    const int nmb = (mv + 15) >> 4;
+    switch ((nmb + 1) >> 1) {  // live blocks rounded up to an even count
+      case 8: big5_tile<16, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 7: big5_tile<14, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 6: big5_tile<12, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 5: big5_tile<10, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 4: big5_tile<8, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 3: big5_tile<6, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 2: big5_tile<4, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      default: big5_tile<2, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+    }
+    __syncthreads();
+  }
+}
+
 static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st);
 
 static int device_cus() {
@@ -642,6 +1140,30 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   const long long ub8 = (ub + 7) / 8 * 8;
   if (grid > ub8) grid = ub8;
   grid = (grid + 7) / 8 * 8;
+  bool k128 = true;  // the 4-stage kernel consumes 4 k-steps of 32 per iteration
+  for (int i = 0; i < fl.ngroups; ++i) k128 = k128 && fl.g[i].K % 128 == 0;
+  // measured on the V3-shaped prefill layer: the 4-stage pipeline wins on the
+  // long-K gate/up phase (K = hidden), the 2-stage one on the down phase
+  // (K = expert width, fewer k-steps per tile to amortise the deeper fill)
+  k128 = k128 && phase == 0;
+#ifdef MOE_FFN_BIG5
+  if (fl.g[0].K % kBK4 == 0 && (fl.ngroups < 2 || fl.g[1].K % kBK4 == 0)) {
+    if (phase == 0)
+      ffn_big5_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    else
+      ffn_big5_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    return hipGetLastError();
+  }
+#endif
+#ifndef MOE_FFN_NO_BIG4
+  if (k128) {
+    if (phase == 0)
+      ffn_big4_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    else
+      ffn_big4_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    return hipGetLastError();
+  }
+#endif
   if (phase == 0)
     ffn_big_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
   else
