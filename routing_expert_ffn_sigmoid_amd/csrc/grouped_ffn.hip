@@ -406,6 +406,22 @@ __device__ __forceinline__ int big_wblock(int wn, int nb) {
   return wn * 4 + nb;
 }
 
+// Fragment reads of the large-tile kernels: the four weight fragments and
+// the first kReadAhead activation fragments first, then per M-block two
+// MFMAs, the read of the fragment kReadAhead blocks ahead, two MFMAs, so the
+// LDS latency of a fragment is covered by the MFMAs of earlier blocks.
+constexpr int kReadAhead = 2;
+template <int NMBW>
+__device__ __forceinline__ void fragment_issue_order() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + (kReadAhead < NMBW ? kReadAhead : NMBW), 0);
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    if (j + kReadAhead < NMBW) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
 template <int NMBW, bool SWIGLU>
 __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
                                             const bf16_t* __restrict__ Bb, f32x4 (&acc)[8][4],
@@ -424,13 +440,20 @@ __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK));
+    bf16x8 af[NMBW];
+#pragma unroll
+    for (int j = 0; j < kReadAhead && j < NMBW; ++j)
+      af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK));
 #pragma unroll
     for (int j = 0; j < NMBW; ++j) {
-      const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK));
+      if (j + kReadAhead < NMBW)
+        af[j + kReadAhead] =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (j + kReadAhead) * 32 * kBK));
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af, acc[j][nb], 0, 0, 0);
+        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
     }
+    fragment_issue_order<NMBW>();
   }
 }
 
@@ -672,13 +695,20 @@ __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
     bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK4));
+  bf16x8 af[NMBW];
+#pragma unroll
+  for (int j = 0; j < kReadAhead && j < NMBW; ++j)
+    af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK4));
 #pragma unroll
   for (int j = 0; j < NMBW; ++j) {
-    const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK4));
+    if (j + kReadAhead < NMBW)
+      af[j + kReadAhead] =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (j + kReadAhead) * 32 * kBK4));
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
-      acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af, acc[j][nb], 0, 0, 0);
+      acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
   }
+  fragment_issue_order<NMBW>();
 }
 
 template <int NMBW, bool SWIGLU>
