@@ -53,6 +53,9 @@ def lib():
         L.orc_route.restype = _i
         L.orc_route.argtypes = [ctypes.POINTER(RouteCfg), _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp]
+        L.orc_dispatch_grouped.restype = _i
+        L.orc_dispatch_grouped.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp]
         L.orc_dispatch.restype = _i
         L.orc_dispatch.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp]
@@ -138,6 +141,28 @@ def dispatch(topk_idx: np.ndarray, topk_score: np.ndarray, N: int,
                             _ptr(inv_row), _ptr(drops))
     if rc != 0:
         raise ValueError("oracle dispatch: invalid input")
+    M = int(offsets[N])
+    return dict(counts=counts, offsets=offsets, row_token=row_token[:M].copy(),
+                inv_row=inv_row, n_dropped=int(drops[0]),
+                n_tok_all_dropped=int(drops[1]))
+
+
+def dispatch_grouped(topk_idx: np.ndarray, topk_score: np.ndarray, N: int, G: int,
+                     group_cap: int) -> dict:
+    """Dispatch with device-level token dropping (group_cap > 0 per group)."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    topk_score = np.ascontiguousarray(topk_score, dtype=np.float32)
+    T, k = topk_idx.shape
+    counts = np.empty((N,), np.int32)
+    offsets = np.empty((N + 1,), np.int32)
+    row_token = np.full((max(T * k, 1),), -1, np.int32)
+    inv_row = np.empty((T, k), np.int32)
+    drops = np.zeros((2,), np.int64)
+    rc = lib().orc_dispatch_grouped(T, N, k, G, group_cap, _ptr(topk_idx), _ptr(topk_score),
+                                    _ptr(counts), _ptr(offsets), _ptr(row_token),
+                                    _ptr(inv_row), _ptr(drops))
+    if rc != 0:
+        raise ValueError("oracle dispatch_grouped: invalid input")
     M = int(offsets[N])
     return dict(counts=counts, offsets=offsets, row_token=row_token[:M].copy(),
                 inv_row=inv_row, n_dropped=int(drops[0]),

@@ -281,6 +281,91 @@ int orc_dispatch(int T, int N, int k, int capacity, const int32_t* topk_idx,
   return 0;
 }
 
+/* Device-level token drop ([EVO] §DeepSeek-v2, device-level token dropping):
+ * experts are split into G equal groups (one group per device); a group
+ * whose assignments exceed `group_cap` keeps the group_cap assignments with
+ * the highest scores and drops the rest.  Order among equal scores: lower
+ * token first, then lower expert.  Rows are laid out expert by expert, token
+ * order inside an expert, as in orc_dispatch. */
+typedef struct {
+  float s;
+  int t, e;
+  int64_t slot;
+} drop_cand_t;
+
+static int drop_cand_cmp(const void* a, const void* b) {
+  const drop_cand_t* x = (const drop_cand_t*)a;
+  const drop_cand_t* y = (const drop_cand_t*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  if (x->t != y->t) return x->t < y->t ? -1 : 1;
+  return (x->e < y->e) ? -1 : (x->e > y->e);
+}
+
+int orc_dispatch_grouped(int T, int N, int k, int G, int group_cap, const int32_t* topk_idx,
+                         const float* topk_score, int32_t* counts, int32_t* offsets,
+                         int32_t* row_token, int32_t* inv_row, int64_t* drop_stats) {
+  if (T < 0 || N <= 0 || k < 0 || G <= 0 || N % G != 0 || group_cap <= 0) return -1;
+  const int gs = N / G;
+  const int64_t A = (int64_t)T * k;
+  for (int e = 0; e < N; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < A; ++a) {
+    int e = topk_idx[a];
+    if (e < 0 || e >= N) return -1;
+    counts[e]++;
+  }
+  uint8_t* kept = (uint8_t*)malloc(A > 0 ? A : 1);
+  for (int64_t a = 0; a < A; ++a) kept[a] = 1;
+  drop_cand_t* cand = (drop_cand_t*)malloc(sizeof(drop_cand_t) * (A > 0 ? A : 1));
+  int64_t dropped = 0;
+  for (int g = 0; g < G; ++g) {
+    int64_t n = 0;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j) {
+        const int64_t a = (int64_t)t * k + j;
+        const int e = topk_idx[a];
+        if (e / gs != g) continue;
+        cand[n].s = topk_score[a];
+        cand[n].t = t;
+        cand[n].e = e;
+        cand[n].slot = a;
+        ++n;
+      }
+    if (n <= group_cap) continue;
+    qsort(cand, (size_t)n, sizeof(drop_cand_t), drop_cand_cmp);
+    for (int64_t r = group_cap; r < n; ++r) {
+      kept[cand[r].slot] = 0;
+      ++dropped;
+    }
+  }
+  for (int64_t a = 0; a < A; ++a) inv_row[a] = -1;
+  offsets[0] = 0;
+  int r = 0;
+  for (int e = 0; e < N; ++e) {
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j) {
+        const int64_t a = (int64_t)t * k + j;
+        if (topk_idx[a] == e && kept[a]) {
+          row_token[r] = t;
+          inv_row[a] = r;
+          ++r;
+        }
+      }
+    offsets[e + 1] = r;
+  }
+  int64_t all_dropped = 0;
+  for (int t = 0; t < T && k > 0; ++t) {
+    int any = 0;
+    for (int j = 0; j < k; ++j) any |= kept[(int64_t)t * k + j];
+    if (!any) ++all_dropped;
+  }
+  drop_stats[0] = dropped;
+  drop_stats[1] = all_dropped;
+  free(kept);
+  free(cand);
+  return 0;
+}
+
 /* ---------------------------------------------------------------- experts */
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }

@@ -85,6 +85,14 @@ int orc_dispatch(int T, int N, int k, int capacity, const int32_t* topk_idx,
                  const float* topk_score, int32_t* counts, int32_t* offsets,
                  int32_t* row_token, int32_t* inv_row, int64_t* drop_stats);
 
+/* Dispatch with device-level token dropping: the N experts form G equal
+ * groups (devices); a group holding more than group_cap assignments keeps
+ * the group_cap highest-scoring ones (ties: lower token, then lower expert).
+ * Outputs as orc_dispatch (counts before dropping).  Returns 0 or -1. */
+int orc_dispatch_grouped(int T, int N, int k, int G, int group_cap, const int32_t* topk_idx,
+                         const float* topk_score, int32_t* counts, int32_t* offsets,
+                         int32_t* row_token, int32_t* inv_row, int64_t* drop_stats);
+
 /* One SwiGLU expert on one row: y = Wd (silu(Wg x) * (Wu x)).
  * w13 (typed) [2I,H]: rows [0,I) gate, rows [I,2I) up; w2 (typed) [H,I]. */
 void orc_swiglu_row(int H, int I, const void* x_row, int x_dtype,

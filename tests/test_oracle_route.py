@@ -216,3 +216,51 @@ def test_v3_group_shape_golden():
     n_cand = r["kept_groups"].sum(1) * (N // G)
     assert np.all(n_cand == gold["candidates"])
     assert r["topk_idx"].shape[1] == gold["topk"]
+
+
+# ------------------------------------------------- v2 device-limited routing
+
+def _walk_down_devices(keys, gs, M, k):
+    """Device-limited routing as the DeepSeek-v2 passage words it: walk the
+    experts from the highest key down, collecting the devices they sit on
+    until M distinct devices are found; then take the top k keys among all
+    experts of those devices (ties: lower index first)."""
+    order = sorted(range(len(keys)), key=lambda e: (-keys[e], e))
+    devices = []
+    for e in order:
+        d = e // gs
+        if d not in devices:
+            devices.append(d)
+        if len(devices) == M:
+            break
+    cands = [e for e in range(len(keys)) if e // gs in devices]
+    cands.sort(key=lambda e: (-keys[e], e))
+    return cands[:k], set(devices)
+
+
+@pytest.mark.parametrize("N,G,M,k", [(16, 4, 2, 3), (24, 8, 3, 6), (160, 8, 3, 6), (32, 8, 1, 4)])
+@pytest.mark.parametrize("score_fn", [oracle.SIGMOID, oracle.SOFTMAX])
+def test_device_limited_routing_is_top1_group_score(N, G, M, k, score_fn):
+    # "DeepSeek MoE：从v1到v3的演进" §DeepSeek-v2 (device-limited routing):
+    # the groups kept by a top-1 group score are the devices the walk-down
+    # collects, with integer-valued logits so that ties occur
+    rng = np.random.default_rng(7 * N + M + score_fn)
+    T = 60
+    logits = rng.integers(-4, 5, size=(T, N)).astype(np.float32)
+    bias = None
+    if score_fn == oracle.SIGMOID:
+        bias = (rng.integers(-2, 3, size=N) * 0.25).astype(np.float32)
+    r = oracle.route(logits, bias, k, n_groups=G, topk_groups=M, group_topn=1,
+                     score_fn=score_fn, norm_topk=0)
+    gs = N // G
+    for t in range(T):
+        if score_fn == oracle.SIGMOID:
+            s = oracle.sigmoid32(logits[t])
+            keys = [float(np.float32(s[e]) + np.float32(bias[e])) for e in range(N)]
+        else:
+            keys = [float(v) for v in logits[t]]
+        chosen, devs = _walk_down_devices(keys, gs, M, k)
+        assert list(r["topk_idx"][t]) == chosen, t
+        assert set(np.nonzero(r["kept_groups"][t])[0]) == devs
+        # fan-out bound: a token reaches at most M devices
+        assert len({e // gs for e in r["topk_idx"][t]}) <= M
