@@ -79,6 +79,12 @@ typedef struct {
   int32_t act_dtype;   /* moe_dtype of x, expert activations and out            */
   int32_t w_dtype;     /* moe_dtype of expert weights (must equal act_dtype)    */
   int32_t router_dtype;/* moe_dtype of the router weight W_g                    */
+  int32_t group_capacity; /* device-level token dropping ([EVO] §DeepSeek-v2):
+                           * each of the n_groups expert groups (devices) keeps
+                           * at most this many assignments, dropping its
+                           * lowest-scored ones; 0 = off, -1 = the average
+                           * group load ceil(T*k / n_groups).  Exclusive with
+                           * `capacity`.                                        */
 } moe_cfg;
 
 /* Layer weights (device pointers):
@@ -161,23 +167,33 @@ moe_status moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  * Selection keys: sigmoid -> fl32(s + b) with s from the library's fp32
  * sigmoid (Cody-Waite reduction, degree-7 Taylor series, correctly rounded
  * add and divide); softmax -> fl32(l + b).  Group score = fl32 sum of the
- * group's group_topn largest keys.  Workspace: moe_workspace_size. */
+ * group's group_topn largest keys.  group_topn = 1 is DeepSeek-v2's
+ * device-limited routing ([EVO] §DeepSeek-v2): with one group per device,
+ * the kept groups are exactly the devices met first when walking the
+ * experts from the highest key down, so a token reaches at most
+ * topk_groups devices.  Workspace: moe_workspace_size. */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
                      float* logits, const float* bias, int32_t* topk_idx,
                      float* topk_gate, float* topk_score, float* token_lse,
                      void* ws, size_t ws_bytes, void* stream);
 
-/* Dispatch ([EVO] §GShard expert capacity; §DeepSeek-v2 drops the
- * lowest-scored tokens first): per-expert counts, optional capacity drop,
- * permutation.  Rows are grouped by expert (ascending), ascending token
- * order inside an expert.  With capacity C > 0 an expert keeps its C
- * assignments of highest topk_score (lower token first on ties).
+/* Dispatch ([EVO] §GShard expert capacity; §DeepSeek-v2 device-level
+ * dropping, lowest-scored tokens first): per-expert counts, optional
+ * dropping, permutation.  Rows are grouped by expert (ascending), ascending
+ * token order inside an expert.
+ *   capacity C > 0: an expert keeps its C assignments of highest topk_score;
+ *   group_capacity: each group of N/n_groups consecutive experts keeps its
+ *   cap highest-scored assignments (cap = group_capacity, or the average
+ *   group load ceil(T*k/n_groups) for -1).
+ * Order among equal scores: lower token first, then lower expert.  The
+ * decision uses topk_score exactly as given (fp32).
  *   topk_idx, topk_score [T,k]; x [T,H] act_dtype or NULL
- *   counts [N] i32 (before capacity), offsets [N+1] i32 (after capacity),
+ *   counts [N] i32 (before dropping), offsets [N+1] i32 (after dropping),
  *   row_token [T*k] i32, inv_row [T,k] i32 (-1 = dropped),
  *   x_perm [T*k, H] act_dtype or NULL: x_perm[r] = x[row_token[r]] for
- *   r < offsets[N]; n_dropped [2] i32 or NULL.
- * Softmax scores with capacity > 0 are MOE_ERR_UNSUPPORTED. */
+ *   r < offsets[N]; n_dropped [2] i32 or NULL: dropped assignments, tokens
+ *   with every assignment dropped.
+ * Dropping needs T < 2^24 (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx,
                        const float* topk_score, const void* x, int32_t* counts,
                        int32_t* offsets, int32_t* row_token, int32_t* inv_row,

@@ -42,7 +42,8 @@ class MoeCfg(ctypes.Structure):
                 ("n_groups", _i32), ("topk_groups", _i32), ("group_topn", _i32),
                 ("score_fn", _i32), ("norm_topk", _i32), ("route_scale", ctypes.c_float),
                 ("capacity", _i32), ("I", _i32), ("n_shared", _i32), ("I_shared", _i32),
-                ("act_dtype", _i32), ("w_dtype", _i32), ("router_dtype", _i32)]
+                ("act_dtype", _i32), ("w_dtype", _i32), ("router_dtype", _i32),
+                ("group_capacity", _i32)]
 
 
 class MoeWeights(ctypes.Structure):

@@ -3,7 +3,13 @@
 //
 // Sources: "DeepSeek MoE：从v1到v3的演进" §GShard (tokens are sent to the
 // experts that own them; expert capacity; overflow passes through the
-// residual) and §DeepSeek-v2 (the lowest-scored tokens are the ones dropped).
+// residual) and §DeepSeek-v2 (device-level dropping: a device over the
+// average load drops its lowest-scored tokens).
+//
+// Dropping order: a 64-bit key per assignment, higher is kept first:
+// order key of the fp32 score (bits 63..32), then the lower token (bits
+// 31..8, T < 2^24), then the lower expert (bits 7..0, N <= 256).  Keys are
+// distinct, so "the C largest keys" is a set of exactly C assignments.
 //
 // Rows are laid out expert by expert, ascending token order inside an
 // expert.  A token's rank inside its expert comes from LDS bit masks: wave w
@@ -20,20 +26,24 @@ int dispatch_blocks(int T) { return (T + kTokPerBlock - 1) / kTokPerBlock; }
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t dispatch_ws_bytes(int T, int N, int k, int capacity) {
+size_t dispatch_ws_bytes(int T, int N, int k, const DropPolicy& d) {
   const size_t nb = dispatch_blocks(T);
   size_t b = 0;
   b += align256(nb * N * sizeof(int32_t));  // block_counts
   b += align256(nb * N * sizeof(int32_t));  // block_base
   b += align256(N * sizeof(int32_t));       // pre_off
-  if (capacity > 0) {
+  if (d.any()) {
     b += align256(static_cast<size_t>(T) * k * sizeof(uint64_t));
     b += align256(static_cast<size_t>(T) * k * sizeof(int32_t));
+  }
+  if (d.group_cap > 0) {
+    b += align256(static_cast<size_t>(d.n_groups) * sizeof(uint64_t));
+    b += align256(N * sizeof(int32_t));
   }
   return b;
 }
 
-DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, int capacity) {
+DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, const DropPolicy& d) {
   const size_t nb = dispatch_blocks(T);
   char* p = static_cast<char*>(ws);
   DispatchWs w{};
@@ -43,12 +53,24 @@ DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, int capacity) {
   p += align256(nb * N * sizeof(int32_t));
   w.pre_off = reinterpret_cast<int32_t*>(p);
   p += align256(N * sizeof(int32_t));
-  if (capacity > 0) {
+  if (d.any()) {
     w.cand_key = reinterpret_cast<uint64_t*>(p);
     p += align256(static_cast<size_t>(T) * k * sizeof(uint64_t));
     w.cand_slot = reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(T) * k * sizeof(int32_t));
+  }
+  if (d.group_cap > 0) {
+    w.group_tau = reinterpret_cast<uint64_t*>(p);
+    p += align256(static_cast<size_t>(d.n_groups) * sizeof(uint64_t));
+    w.kept = reinterpret_cast<int32_t*>(p);
   }
   return w;
+}
+
+__device__ __forceinline__ uint64_t drop_key(float s, int t, int e) {
+  return (static_cast<uint64_t>(f32_order_key(s)) << 32) |
+         (static_cast<uint64_t>(0xFFFFFFu - static_cast<uint32_t>(t)) << 8) |
+         static_cast<uint64_t>(0xFFu - static_cast<uint32_t>(e));
 }
 
 // Build mask[w][e] for this block's tokens.  masks: [4][N] in LDS.
@@ -138,7 +160,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score, int T, int N,
-    int k, int capacity, const int32_t* __restrict__ block_base,
+    int k, int capacity, bool all_candidates, const int32_t* __restrict__ block_base,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pre_off, int32_t* __restrict__ row_token,
     int32_t* __restrict__ inv_row, uint64_t* __restrict__ cand_key,
@@ -160,74 +182,70 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int rank = block_base[static_cast<int64_t>(blockIdx.x) * N + e];
     for (int w2 = 0; w2 < w; ++w2) rank += __popcll(masks[w2 * N + e]);
     rank += __popcll(masks[w * N + e] & below);
-    if (capacity == 0 || counts[e] <= capacity) {
+    if (!all_candidates && (capacity == 0 || counts[e] <= capacity)) {
       const int row = offsets[e] + rank;
       inv_row[slot] = row;
       row_token[row] = t;
     } else {
+      // candidates of an expert sit in token order at pre_off[e] + rank
       const int pos = pre_off[e] + rank;
-      cand_key[pos] = (static_cast<uint64_t>(f32_order_key(topk_score[slot])) << 32) |
-                      (0xffffffffu - static_cast<uint32_t>(t));
+      cand_key[pos] = drop_key(topk_score[slot], t, e);
       cand_slot[pos] = static_cast<int32_t>(slot);
     }
   }
 }
 
-// One workgroup per expert over capacity.  Finds the capacity-th largest
-// 64-bit key (score order key, then lower token) by an 8-bit radix select,
-// then keeps every key >= it, in token order.
+// The `need`-th largest of n distinct 64-bit keys, by an 8-bit radix select
+// over the whole workgroup (result in every thread).
 constexpr int kCapThreads = 1024;
 
-__global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ pre_off, const uint64_t* __restrict__ cand_key,
-    const int32_t* __restrict__ cand_slot, int k, int capacity,
-    int32_t* __restrict__ row_token, int32_t* __restrict__ inv_row) {
-  const int e = blockIdx.x;
-  const int c = counts[e];
-  if (c <= capacity) return;  // uniform
+__device__ uint64_t radix_select_key(const uint64_t* __restrict__ keys, int n, int need) {
   __shared__ int hist[256];
   __shared__ unsigned long long sh_prefix;
   __shared__ int sh_need;
-  __shared__ int scan[kCapThreads];
-  const uint64_t* keys = cand_key + pre_off[e];
-  const int32_t* slots = cand_slot + pre_off[e];
-
   if (threadIdx.x == 0) {
     sh_prefix = 0ull;
-    sh_need = capacity;
+    sh_need = need;
   }
   for (int d = 7; d >= 0; --d) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     const uint64_t prefix = sh_prefix;
     const int hs = 8 * (d + 1);
-    for (int i = threadIdx.x; i < c; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint64_t key = keys[i];
       const bool match = (d == 7) || ((key >> hs) == (prefix >> hs));
       if (match) atomicAdd(&hist[(key >> (8 * d)) & 255], 1);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      int need = sh_need;
+      int left = sh_need;
       int cum = 0;
       int digit = 0;
       for (int v = 255; v >= 0; --v) {
-        if (cum + hist[v] >= need) {
+        if (cum + hist[v] >= left) {
           digit = v;
           break;
         }
         cum += hist[v];
       }
-      sh_need = need - cum;
+      sh_need = left - cum;
       sh_prefix = prefix | (static_cast<uint64_t>(digit) << (8 * d));
     }
     __syncthreads();
   }
   const uint64_t tau = sh_prefix;
+  __syncthreads();
+  return tau;
+}
 
-  // keep keys >= tau (exactly `capacity` of them: keys are distinct)
-  const int base_row = offsets[e];
+// Rows for one expert's candidates (token order): keys >= tau are kept and
+// numbered from base_row in token order, the others are dropped.
+__device__ void assign_kept_rows(const uint64_t* __restrict__ keys,
+                                 const int32_t* __restrict__ slots, int c, uint64_t tau,
+                                 int base_row, int k, int32_t* __restrict__ row_token,
+                                 int32_t* __restrict__ inv_row) {
+  __shared__ int scan[kCapThreads];
   int running = 0;
   for (int c0 = 0; c0 < c; c0 += kCapThreads) {
     const int i = c0 + threadIdx.x;
@@ -257,6 +275,83 @@ __global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
   }
 }
 
+// Per-expert capacity: one workgroup per expert over capacity keeps its
+// `capacity` largest keys.
+__global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pre_off, const uint64_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_slot, int k, int capacity,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ inv_row) {
+  const int e = blockIdx.x;
+  const int c = counts[e];
+  if (c <= capacity) return;  // uniform
+  const uint64_t* keys = cand_key + pre_off[e];
+  const uint64_t tau = radix_select_key(keys, c, capacity);
+  assign_kept_rows(keys, cand_slot + pre_off[e], c, tau, offsets[e], k, row_token, inv_row);
+}
+
+// Device-level dropping, step 1: one workgroup per group of gs experts.  The
+// group's candidates are contiguous (experts in order); a group over its cap
+// finds the cap-th largest key, and every expert of the group counts its
+// candidates at or above it.
+__global__ __launch_bounds__(kCapThreads) void group_select_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ pre_off,
+    const uint64_t* __restrict__ cand_key, int gs, int group_cap,
+    uint64_t* __restrict__ group_tau, int32_t* __restrict__ kept) {
+  __shared__ int kc[256];
+  const int g = blockIdx.x;
+  const int e0 = g * gs;
+  const int begin = pre_off[e0];
+  const int end = pre_off[e0 + gs - 1] + counts[e0 + gs - 1];
+  const int n = end - begin;
+  uint64_t tau = 0ull;
+  if (n > group_cap) tau = radix_select_key(cand_key + begin, n, group_cap);  // uniform branch
+  for (int i = threadIdx.x; i < gs; i += blockDim.x) kc[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint64_t key = cand_key[begin + i];
+    if (key >= tau) atomicAdd(&kc[0xFF - static_cast<int>(key & 0xFF) - e0], 1);  // integer: order-free
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < gs; i += blockDim.x) kept[e0 + i] = kc[i];
+  if (threadIdx.x == 0) group_tau[g] = tau;
+}
+
+// Step 2 (one workgroup of 256, thread e = expert e): row offsets from the
+// kept counts, and the dropped-assignment count.
+__global__ __launch_bounds__(256) void kept_scan_kernel(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ kept, int N,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ n_dropped) {
+  __shared__ int sh[256];
+  const int e = threadIdx.x;
+  const int ke = e < N ? kept[e] : 0;
+  const int de = e < N ? counts[e] - ke : 0;
+  const int incl = block_scan_incl(ke, sh);
+  const int drop_tot = block_scan_incl(de, sh);
+  if (e < N) offsets[e] = incl - ke;
+  if (e == N - 1) {
+    offsets[N] = incl;
+    if (n_dropped) {
+      n_dropped[0] = drop_tot;
+      n_dropped[1] = 0;
+    }
+  }
+}
+
+// Step 3: one workgroup per expert numbers its kept candidates.
+__global__ __launch_bounds__(kCapThreads) void group_assign_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pre_off, const uint64_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_slot, const uint64_t* __restrict__ group_tau, int gs, int k,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ inv_row) {
+  const int e = blockIdx.x;
+  const int c = counts[e];
+  if (c == 0) return;  // uniform
+  assign_kept_rows(cand_key + pre_off[e], cand_slot + pre_off[e], c, group_tau[e / gs],
+                   offsets[e], k, row_token, inv_row);
+}
+
 __global__ __launch_bounds__(256) void count_all_dropped_kernel(const int32_t* __restrict__ inv_row,
                                                                 int T, int k,
                                                                 int32_t* __restrict__ n_dropped) {
@@ -284,28 +379,39 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
 }
 
 hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
-                           int k, int capacity, int32_t* counts, int32_t* offsets,
+                           int k, const DropPolicy& d, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
                            const DispatchWs& w, hipStream_t st) {
   const int nb = dispatch_blocks(T);
   const size_t lds = 4 * N * sizeof(unsigned long long);
+  const bool grouped = d.group_cap > 0;
   if (nb > 0 && k > 0)
     dispatch_count_kernel<<<nb, 256, lds, st>>>(topk_idx, T, N, k, w.block_counts);
   else if (nb > 0)
     fill_i32_kernel<<<(nb * N + 255) / 256, 256, 0, st>>>(w.block_counts, nb * N, 0);
-  dispatch_scan_kernel<<<1, 256, 0, st>>>(w.block_counts, nb, N, capacity, w.block_base,
-                                          counts, offsets, w.pre_off, n_dropped);
+  // with group dropping the offsets and drop counts written here are
+  // provisional (no drops); kept_scan_kernel overwrites them
+  dispatch_scan_kernel<<<1, 256, 0, st>>>(w.block_counts, nb, N, grouped ? 0 : d.capacity,
+                                          w.block_base, counts, offsets, w.pre_off, n_dropped);
   if (nb > 0 && k > 0) {
-    dispatch_scatter_kernel<<<nb, 256, lds, st>>>(topk_idx, topk_score, T, N, k, capacity,
-                                                  w.block_base, counts, offsets, w.pre_off,
-                                                  row_token, inv_row, w.cand_key, w.cand_slot);
-    if (capacity > 0) {
+    dispatch_scatter_kernel<<<nb, 256, lds, st>>>(
+        topk_idx, topk_score, T, N, k, grouped ? 0 : d.capacity, grouped, w.block_base, counts,
+        offsets, w.pre_off, row_token, inv_row, w.cand_key, w.cand_slot);
+    if (grouped) {
+      const int gs = N / d.n_groups;
+      group_select_kernel<<<d.n_groups, kCapThreads, 0, st>>>(counts, w.pre_off, w.cand_key, gs,
+                                                               d.group_cap, w.group_tau, w.kept);
+      kept_scan_kernel<<<1, 256, 0, st>>>(counts, w.kept, N, offsets, n_dropped);
+      group_assign_kernel<<<N, kCapThreads, 0, st>>>(counts, offsets, w.pre_off, w.cand_key,
+                                                     w.cand_slot, w.group_tau, gs, k, row_token,
+                                                     inv_row);
+    } else if (d.capacity > 0) {
       capacity_select_kernel<<<N, kCapThreads, 0, st>>>(counts, offsets, w.pre_off, w.cand_key,
-                                                        w.cand_slot, k, capacity, row_token,
+                                                        w.cand_slot, k, d.capacity, row_token,
                                                         inv_row);
-      if (n_dropped)
-        count_all_dropped_kernel<<<(T + 255) / 256, 256, 0, st>>>(inv_row, T, k, n_dropped);
     }
+    if (d.any() && n_dropped)
+      count_all_dropped_kernel<<<(T + 255) / 256, 256, 0, st>>>(inv_row, T, k, n_dropped);
   }
   return hipGetLastError();
 }

@@ -36,9 +36,27 @@ moe_status check_cfg(const moe_cfg* c) {
   if (c->H % 64 != 0 || c->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && (static_cast<long long>(c->n_shared) * c->I_shared) % 64 != 0)
     return MOE_ERR_UNSUPPORTED;
+  if (c->group_capacity < -1) return MOE_ERR_INVALID_ARG;
+  if (c->group_capacity != 0 && c->capacity > 0) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != c->w_dtype) return MOE_ERR_UNSUPPORTED;
-  if (c->score_fn == MOE_SCORE_SOFTMAX && c->capacity > 0) return MOE_ERR_UNSUPPORTED;
+  // dropping keys hold the token index in 24 bits
+  if ((c->capacity > 0 || c->group_capacity != 0) && c->T >= (1 << 24)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// The dropping policy a configuration stands for.
+DropPolicy drop_policy(const moe_cfg* c) {
+  DropPolicy d{};
+  d.capacity = c->capacity;
+  d.n_groups = c->n_groups;
+  if (c->group_capacity > 0) {
+    d.group_cap = c->group_capacity;
+  } else if (c->group_capacity == -1) {  // average group load, rounded up
+    const long long tk = static_cast<long long>(c->T) * c->k;
+    d.group_cap = static_cast<int>((tk + c->n_groups - 1) / c->n_groups);
+  }
+  if (d.group_cap <= 0) d.group_cap = 0;  // no assignments: nothing to drop
+  return d;
 }
 
 struct LayerLayout {
@@ -68,7 +86,7 @@ LayerLayout layout(const moe_cfg* c) {
   L.counts = take(N * 4);
   L.offsets = take((N + 1) * 4);
   L.ndrop = take(2 * 4);
-  L.disp = take(dispatch_ws_bytes(c->T, c->N, c->k, c->capacity));
+  L.disp = take(dispatch_ws_bytes(c->T, c->N, c->k, drop_policy(c)));
   L.row_token = take(TK * 4);
   L.inv_row = take(TK * 4);
   L.h_r = take(TK * c->I * es);
@@ -229,12 +247,13 @@ moe_status moe_permute(const moe_cfg* cfg, const int32_t* topk_idx, const float*
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
   if (TK > 0 && (!topk_idx || !topk_score || !row_token || !inv_row)) return MOE_ERR_INVALID_ARG;
   if (x_perm && !x) return MOE_ERR_INVALID_ARG;
-  const size_t need = dispatch_ws_bytes(cfg->T, cfg->N, cfg->k, cfg->capacity);
+  const DropPolicy dp = drop_policy(cfg);
+  const size_t need = dispatch_ws_bytes(cfg->T, cfg->N, cfg->k, dp);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  DispatchWs w = dispatch_ws_carve(ws, cfg->T, cfg->N, cfg->k, cfg->capacity);
-  MOE_TRY(launch_dispatch(topk_idx, topk_score, cfg->T, cfg->N, cfg->k, cfg->capacity, counts,
-                          offsets, row_token, inv_row, n_dropped, w, st));
+  DispatchWs w = dispatch_ws_carve(ws, cfg->T, cfg->N, cfg->k, dp);
+  MOE_TRY(launch_dispatch(topk_idx, topk_score, cfg->T, cfg->N, cfg->k, dp, counts, offsets,
+                          row_token, inv_row, n_dropped, w, st));
   if (x_perm && TK > 0)
     MOE_TRY(launch_permute(x, static_cast<int>(esize(cfg->act_dtype)), cfg->H, row_token, offsets,
                            cfg->N, static_cast<int>(TK), x_perm, st));
@@ -367,9 +386,10 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
   MOE_TRY(launch_route(p, st));
   // 3. dispatch (the row gather itself is fused into the gate/up loads)
   record(aux, MOE_STAGE_DISPATCH, st);
-  DispatchWs dw = dispatch_ws_carve(at<char>(ws, L.disp), T, N, k, cfg->capacity);
-  MOE_TRY(launch_dispatch(idx, score, T, N, k, cfg->capacity, counts, offsets, row_token, inv_row,
-                          ndrop, dw, st));
+  const DropPolicy dp = drop_policy(cfg);
+  DispatchWs dw = dispatch_ws_carve(at<char>(ws, L.disp), T, N, k, dp);
+  MOE_TRY(launch_dispatch(idx, score, T, N, k, dp, counts, offsets, row_token, inv_row, ndrop, dw,
+                          st));
   // 4. experts
   void* y_r = at<char>(ws, L.y_r);
   void* y_s = cfg->n_shared > 0 ? at<char>(ws, L.y_s) : nullptr;

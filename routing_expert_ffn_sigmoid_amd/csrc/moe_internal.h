@@ -124,18 +124,29 @@ struct RouteParams {
 };
 hipError_t launch_route(const RouteParams& p, hipStream_t st);
 
+// Dropping policy of one dispatch: per-expert capacity, or a cap per group
+// of n_groups consecutive experts (device-level dropping); at most one set.
+struct DropPolicy {
+  int capacity;   // per expert, 0 = none
+  int n_groups;   // groups for group_cap
+  int group_cap;  // per group, 0 = none (already resolved, > 0 when set)
+  bool any() const { return capacity > 0 || group_cap > 0; }
+};
+
 struct DispatchWs {
   int32_t* block_counts;  // [nb][N]
   int32_t* block_base;    // [nb][N]
   int32_t* pre_off;       // [N]
-  uint64_t* cand_key;     // [T*k] (capacity only)
-  int32_t* cand_slot;     // [T*k] (capacity only)
+  uint64_t* cand_key;     // [T*k] (dropping only)
+  int32_t* cand_slot;     // [T*k] (dropping only)
+  uint64_t* group_tau;    // [n_groups] (group dropping only)
+  int32_t* kept;          // [N] (group dropping only)
 };
 int dispatch_blocks(int T);
-size_t dispatch_ws_bytes(int T, int N, int k, int capacity);
-DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, int capacity);
+size_t dispatch_ws_bytes(int T, int N, int k, const DropPolicy& d);
+DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, const DropPolicy& d);
 hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
-                           int k, int capacity, int32_t* counts, int32_t* offsets,
+                           int k, const DropPolicy& d, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
                            const DispatchWs& w, hipStream_t st);
 hipError_t launch_permute(const void* x, int elem_bytes, int H, const int32_t* row_token,

@@ -8,8 +8,13 @@ Shapes follow the pages:
   * v1: softmax gate, fine-grained routed experts plus always-on shared
     experts ("DeepSeek MoE：从v1到v3的演进" §DeepSeek-v1).
   * capacity factor and dropping ("DeepSeek MoE：从v1到v3的演进" §GShard).
+  * v2: 160 routed / 6 active experts ("DeepSeek MoE：从v1到v3的演进"
+    §DeepSeek-v3 table), device-limited routing over 8 devices keeping the
+    3 best, and device-level token dropping at the average device load
+    (§DeepSeek-v2).
 Sizes not printed on the pages (hidden, intermediate, token counts, weight
-scales) are the workload definitions of this library's benchmark.
+scales, the v2 device count and kept-device count) are the workload
+definitions of this library's benchmark.
 """
 from __future__ import annotations
 
@@ -45,6 +50,7 @@ class Workload:
     bias_kind: str  # "none" | "uniform" | "zipf"
     bias_param: float  # half-width of the uniform bias, or the Zipf exponent
     seed: int = 0
+    group_capacity: int = 0  # device-level drop: 0 off, -1 average group load
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -89,9 +95,27 @@ V3_SKEW = V3_PREFILL.with_(
     name="v3_skew_bf16_T16384_H7168_N256_k8_G8of4_C640", T=16384,
     capacity=capacity_for(16384, 8, 256), bias_kind="zipf", bias_param=1.2)
 
-PRESETS = {w.name: w for w in (TINY, V1, V3_PREFILL, V3_DECODE, V3_SKEW)}
-SHORT = {"tiny": TINY, "v1": V1, "v3_prefill": V3_PREFILL,
+# v2-shaped routing: softmax gate (raw probability), device-limited routing
+# (group score = the group's best logit, 3 of 8 devices kept), device-level
+# dropping at the average device load; expert widths as v1.
+V2 = Workload(
+    name="v2_bf16_T4096_H2048_N160_k6_dev8of3_drop", T=4096, H=2048, N=160, k=6,
+    n_groups=8, topk_groups=3, group_topn=1, score_fn=SOFTMAX, norm_topk=0,
+    route_scale=1.0, capacity=0, I=1408, n_shared=2, I_shared=1408,
+    act_dtype=BF16, w_dtype=BF16, router_dtype=BF16,
+    x_std=1.0, wg_std=0.006, w_std=0.006, bias_kind="none", bias_param=0.0,
+    group_capacity=-1)
+
+PRESETS = {w.name: w for w in (TINY, V1, V2, V3_PREFILL, V3_DECODE, V3_SKEW)}
+SHORT = {"tiny": TINY, "v1": V1, "v2": V2, "v3_prefill": V3_PREFILL,
          "v3_decode": V3_DECODE, "v3_skew": V3_SKEW}
+
+
+def group_capacity_for(wl: Workload) -> int:
+    """The per-group cap a workload's group_capacity stands for (0 = off)."""
+    if wl.group_capacity >= 0:
+        return wl.group_capacity
+    return (wl.T * wl.k + wl.n_groups - 1) // wl.n_groups
 
 
 def get(name: str) -> Workload:

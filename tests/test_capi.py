@@ -74,7 +74,10 @@ def test_workspace_size_for_presets(name):
     ({"I": 96}, moe.MOE_ERR_UNSUPPORTED),
     ({"N": 16, "n_groups": 8, "topk_groups": 2}, moe.MOE_ERR_UNSUPPORTED),  # groups of 2
     ({"w_dtype": 1}, moe.MOE_ERR_UNSUPPORTED),
-    ({"score_fn": 0, "capacity": 4}, moe.MOE_ERR_UNSUPPORTED),
+    ({"group_capacity": -2}, moe.MOE_ERR_INVALID_ARG),
+    ({"group_capacity": -1, "capacity": 4}, moe.MOE_ERR_INVALID_ARG),  # one policy at a time
+    ({"T": 1 << 24, "capacity": 4}, moe.MOE_ERR_UNSUPPORTED),  # 24-bit token field of the keys
+    ({"T": 1 << 24, "group_capacity": -1}, moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs_rejected_on_host(override, code):
     cfg = moe.make_cfg(workloads.TINY, **override)

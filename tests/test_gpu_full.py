@@ -60,6 +60,16 @@ def test_v1_shaped_layer():
     _run(wl, inp, 24)
 
 
+def test_v2_shaped_layer_device_limited_with_device_drop():
+    """160 experts on 8 devices (3 kept, top-1 group score), softmax gate,
+    dropping at the average device load; sampled rows include dropped ones."""
+    require_gpu()
+    wl = workloads.V2
+    inp = make_inputs(wl)
+    _, _, d = _run(wl, inp, 24, pick_dropped=True)
+    assert d["n_dropped"] > 0
+
+
 def test_v3_prefill_layer(v3_weights):
     wl = workloads.V3_PREFILL
     from routing_expert_ffn_sigmoid_amd import synth
