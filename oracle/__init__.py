@@ -56,6 +56,10 @@ def lib():
         L.orc_dispatch_grouped.restype = _i
         L.orc_dispatch_grouped.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp]
+        L.orc_seq_load_stats.restype = _i
+        L.orc_seq_load_stats.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.orc_group_load_stats.restype = _i
+        L.orc_group_load_stats.argtypes = [_i, _i, _vp, _vp, _vp, _vp, _vp]
         L.orc_dispatch.restype = _i
         L.orc_dispatch.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp]
@@ -242,3 +246,36 @@ def bias_update(counts: np.ndarray, bias: np.ndarray, u: float) -> np.ndarray:
     out = np.empty_like(bias)
     lib().orc_bias_update(counts.shape[0], _ptr(counts), _ptr(bias), u, _ptr(out))
     return out
+
+
+def seq_load_stats(logits: np.ndarray, topk_idx: np.ndarray, cu_seqlens, k: int,
+                   score_fn: int = SIGMOID) -> dict:
+    """Per-sequence f, P, L_B and their mean over non-empty sequences."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, N = logits.shape
+    S = cu.size - 1
+    f = np.zeros((max(S, 1), N), np.float64)
+    P = np.zeros((max(S, 1), N), np.float64)
+    L = np.zeros((max(S, 1),), np.float64)
+    Lm = np.zeros((1,), np.float64)
+    rc = lib().orc_seq_load_stats(T, N, k, score_fn, S, _ptr(cu), _ptr(topk_idx), _ptr(logits),
+                                  _ptr(f), _ptr(P), _ptr(L), _ptr(Lm))
+    if rc != 0:
+        raise ValueError("oracle seq_load_stats: invalid input")
+    return dict(f=f[:S], P=P[:S], L=L[:S], L_mean=float(Lm[0]))
+
+
+def group_load_stats(f: np.ndarray, P: np.ndarray, G: int) -> dict:
+    """Device-level F_g, P_g and L_dev = G * sum F_g P_g."""
+    f = np.ascontiguousarray(f, dtype=np.float64)
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    N = f.size
+    Fg = np.empty((G,), np.float64)
+    Pg = np.empty((G,), np.float64)
+    L = np.zeros((1,), np.float64)
+    rc = lib().orc_group_load_stats(N, G, _ptr(f), _ptr(P), _ptr(Fg), _ptr(Pg), _ptr(L))
+    if rc != 0:
+        raise ValueError("oracle group_load_stats: invalid input")
+    return dict(F=Fg, P=Pg, L_dev=float(L[0]))

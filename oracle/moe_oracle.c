@@ -474,6 +474,71 @@ void orc_load_stats(int T, int N, int k, int score_fn, const float* logits,
   free(col);
 }
 
+/* Sequence-wise balance statistics ([EVO] §DeepSeek-v3, sequence-wise
+ * balance loss: the expert-level statistics of [EVO] §ST-MoE taken over the
+ * tokens of one sequence instead of the whole batch).  Sequence q covers
+ * tokens [cu_seqlens[q], cu_seqlens[q+1]); its counts come from topk_idx.
+ * L_mean = mean of L_seq over the non-empty sequences (0 if none). */
+int orc_seq_load_stats(int T, int N, int k, int score_fn, int n_seq, const int32_t* cu_seqlens,
+                       const int32_t* topk_idx, const float* logits, double* f_seq,
+                       double* P_seq, double* L_seq, double* L_mean) {
+  if (T < 0 || N <= 0 || k < 0 || n_seq < 0) return -1;
+  if (n_seq > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seq] != T)) return -1;
+  for (int q = 0; q < n_seq; ++q)
+    if (cu_seqlens[q + 1] < cu_seqlens[q]) return -1;
+  int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * N);
+  double sum = 0.0;
+  int nonempty = 0;
+  for (int q = 0; q < n_seq; ++q) {
+    const int a = cu_seqlens[q], b = cu_seqlens[q + 1];
+    for (int e = 0; e < N; ++e) counts[e] = 0;
+    for (int64_t i = (int64_t)a * k; i < (int64_t)b * k; ++i) {
+      const int e = topk_idx[i];
+      if (e < 0 || e >= N) {
+        free(counts);
+        return -1;
+      }
+      counts[e]++;
+    }
+    double sc[3];
+    orc_load_stats(b - a, N, k, score_fn, logits + (int64_t)a * N, counts, f_seq + (int64_t)q * N,
+                   P_seq + (int64_t)q * N, sc);
+    L_seq[q] = sc[0];
+    if (b > a) {
+      sum += sc[0];
+      ++nonempty;
+    }
+  }
+  *L_mean = nonempty > 0 ? sum / nonempty : 0.0;
+  free(counts);
+  return 0;
+}
+
+/* Device-level balance statistics ([EVO] §DeepSeek-v1, device-level balance
+ * loss: the experts split into G groups, one per device, balanced at group
+ * granularity).  F_g = sum of f over the group's experts (share of the
+ * assignments), P_g = sum of P (share of the score mass), L_dev =
+ * G * sum_g F_g P_g, which is 1 for a uniform load and, with one expert per
+ * group, the expert-level L_B. */
+int orc_group_load_stats(int N, int G, const double* f, const double* P, double* F_g,
+                         double* P_g, double* L_dev) {
+  if (N <= 0 || G <= 0 || N % G != 0) return -1;
+  const int gs = N / G;
+  double l = 0.0;
+  for (int g = 0; g < G; ++g) {
+    double a = 0.0, b = 0.0;
+    for (int e = g * gs; e < (g + 1) * gs; ++e) {
+      a += f[e];
+      b += P[e];
+    }
+    F_g[g] = a;
+    P_g[g] = b;
+    l += a * b;
+  }
+  *L_dev = G * l;
+  return 0;
+}
+
 /* ---------------------------------------------------------------- bias */
 
 void orc_bias_update(int N, const int32_t* counts, const float* bias_in,

@@ -127,6 +127,20 @@ void orc_load_stats(int T, int N, int k, int score_fn, const float* logits,
                     const int32_t* counts, double* f, double* P,
                     double* scalars);
 
+/* Sequence-wise statistics: orc_load_stats's f, P and L_B over the tokens
+ * [cu_seqlens[q], cu_seqlens[q+1]) of each sequence q (counts from
+ * topk_idx).  f_seq, P_seq [n_seq, N]; L_seq [n_seq]; L_mean = mean of L_seq
+ * over non-empty sequences.  cu_seqlens: n_seq+1 non-decreasing values from
+ * 0 to T.  Returns 0 or -1. */
+int orc_seq_load_stats(int T, int N, int k, int score_fn, int n_seq, const int32_t* cu_seqlens,
+                       const int32_t* topk_idx, const float* logits, double* f_seq,
+                       double* P_seq, double* L_seq, double* L_mean);
+
+/* Device-level statistics over G equal expert groups: F_g = sum f, P_g =
+ * sum P over the group, L_dev = G * sum_g F_g P_g.  Returns 0 or -1. */
+int orc_group_load_stats(int N, int G, const double* f, const double* P, double* F_g,
+                         double* P_g, double* L_dev);
+
 /* Auxiliary-loss-free bias update ([EVO] §DeepSeek-v3):
  * e_i = mean(c) - c_i ; b_i <- b_i + u * sign(e_i), sign(0) = 0.
  * Returned in fp32 (the bias is an fp32 tensor). */
