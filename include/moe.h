@@ -9,7 +9,9 @@
  *   dispatch                -> moe_permute
  *   SwiGLU experts          -> moe_grouped_ffn (routed experts, shared expert)
  *   combine                 -> moe_combine
- *   load statistics         -> moe_load_stats
+ *   load statistics         -> moe_load_stats (batch), moe_seq_load_stats
+ *                              (per sequence), moe_group_load_stats (per
+ *                              expert group / device)
  *   all of the above        -> moe_layer_forward
  *
  * Sources (web pages, cited by title and section):
@@ -245,6 +247,36 @@ moe_status moe_load_stats(const moe_cfg* cfg, const int32_t* counts,
                           const float* token_lse, const float* logits, float* f,
                           float* P, float* scalars, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* Sequence-wise load statistics ([EVO] §DeepSeek-v3, sequence-wise balance
+ * loss; the pages print no formula, so these are moe_load_stats's f, P and
+ * L_B computed over the tokens of one sequence instead of the batch):
+ * sequence q covers tokens [cu_seqlens[q], cu_seqlens[q+1]); its counts come
+ * from topk_idx (before any dropping).
+ *   cu_seqlens [n_seq+1] i32 DEVICE, non-decreasing from 0 to T (values are
+ *            clamped to [0, T]; outputs for other inputs are unspecified);
+ *   topk_idx [T,k] i32, token_lse [T] f32 (needed for softmax), logits [T,N]
+ *   -> f_seq [n_seq,N] f32, P_seq [n_seq,N] f32, L_seq [n_seq] f32, and
+ *   L_mean [1] f32 or NULL: mean of L_seq over the non-empty sequences
+ *   (0 when there are none).  An empty sequence has f = P = 0, L = 0.
+ * fp64 accumulation in a fixed order.  Workspace:
+ * moe_seq_load_stats_workspace_size. */
+moe_status moe_seq_load_stats(const moe_cfg* cfg, int32_t n_seq, const int32_t* cu_seqlens,
+                              const int32_t* topk_idx, const float* token_lse,
+                              const float* logits, float* f_seq, float* P_seq, float* L_seq,
+                              float* L_mean, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_seq_load_stats_workspace_size(const moe_cfg* cfg, int32_t n_seq, size_t* bytes);
+
+/* Device-level load statistics ([EVO] §DeepSeek-v1, device-level balance
+ * loss; no formula printed): the cfg's n_groups groups of consecutive
+ * experts stand for devices; F_g = sum of f over the group (its share of
+ * the assignments), P_g = sum of P (its share of the score mass), L_dev =
+ * n_groups * sum_g F_g P_g (1 when balanced; the expert-level L_B when every
+ * group holds one expert).
+ *   f, P [N] f32 (moe_load_stats outputs) -> F_group [n_groups] f32 or NULL,
+ *   P_group [n_groups] f32 or NULL, L_dev [1] f32 or NULL.  No workspace. */
+moe_status moe_group_load_stats(const moe_cfg* cfg, const float* f, const float* P,
+                                float* F_group, float* P_group, float* L_dev, void* stream);
 
 /* Auxiliary-loss-free bias update ([EVO] §DeepSeek-v3): with c the
  * per-expert counts and cbar their mean, b_e <- b_e + u * sign(cbar - c_e),

@@ -25,6 +25,7 @@ N_STAGES = len(STAGES)
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_load_stats",
+           "moe_seq_load_stats", "moe_seq_load_stats_workspace_size", "moe_group_load_stats",
            "moe_bias_update", "moe_layer_forward", "moe_status_string"]
 
 _vp = ctypes.c_void_p
@@ -88,6 +89,12 @@ def lib():
         L.moe_combine.argtypes = [cfgp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_load_stats.restype = st
         L.moe_load_stats.argtypes = [cfgp] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_seq_load_stats.restype = st
+        L.moe_seq_load_stats.argtypes = [cfgp, _i32] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_seq_load_stats_workspace_size.restype = st
+        L.moe_seq_load_stats_workspace_size.argtypes = [cfgp, _i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_group_load_stats.restype = st
+        L.moe_group_load_stats.argtypes = [cfgp] + [_vp] * 5 + [_vp]
         L.moe_bias_update.restype = st
         L.moe_bias_update.argtypes = [cfgp, _vp, _vp, ctypes.c_float, _vp]
         L.moe_layer_forward.restype = st
@@ -252,6 +259,40 @@ def moe_load_stats(cfg: MoeCfg, counts, token_lse, logits, f, P, scalars, ws, st
         _ptr(P, torch.float32, "P", (N,)), _ptr(scalars, torch.float32, "scalars", (3,)),
         wsp, wsb, _stream(stream))
     _check(code, "moe_load_stats")
+
+
+def moe_seq_load_stats_workspace_size(cfg: MoeCfg, n_seq: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_seq_load_stats_workspace_size(ctypes.byref(cfg), n_seq, ctypes.byref(n)),
+           "moe_seq_load_stats_workspace_size")
+    return n.value
+
+
+def moe_seq_load_stats(cfg: MoeCfg, cu_seqlens, topk_idx, token_lse, logits, f_seq, P_seq,
+                       L_seq, L_mean=None, ws=None, stream=None):
+    torch = _torch()
+    T, N, k = cfg.T, cfg.N, cfg.k
+    S = cu_seqlens.numel() - 1
+    wsp, wsb = _ws(ws)
+    code = lib().moe_seq_load_stats(
+        ctypes.byref(cfg), S, _ptr(cu_seqlens, torch.int32, "cu_seqlens", (S + 1,)),
+        _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
+        _ptr(token_lse, torch.float32, "token_lse", (T,)),
+        _ptr(logits, torch.float32, "logits", (T, N)),
+        _ptr(f_seq, torch.float32, "f_seq", (S, N)), _ptr(P_seq, torch.float32, "P_seq", (S, N)),
+        _ptr(L_seq, torch.float32, "L_seq", (S,)), _ptr(L_mean, torch.float32, "L_mean", (1,)),
+        wsp, wsb, _stream(stream))
+    _check(code, "moe_seq_load_stats")
+
+
+def moe_group_load_stats(cfg: MoeCfg, f, P, F_group=None, P_group=None, L_dev=None, stream=None):
+    torch = _torch()
+    N, G = cfg.N, cfg.n_groups
+    code = lib().moe_group_load_stats(
+        ctypes.byref(cfg), _ptr(f, torch.float32, "f", (N,)), _ptr(P, torch.float32, "P", (N,)),
+        _ptr(F_group, torch.float32, "F_group", (G,)), _ptr(P_group, torch.float32, "P_group", (G,)),
+        _ptr(L_dev, torch.float32, "L_dev", (1,)), _stream(stream))
+    _check(code, "moe_group_load_stats")
 
 
 def moe_bias_update(cfg: MoeCfg, counts, bias, u: float, stream=None):

@@ -200,6 +200,188 @@ hipError_t launch_stats(const int32_t* counts, const float* lse, const float* lo
   return hipGetLastError();
 }
 
+// ------------------------------------------------- sequence-wise stats
+// The load statistics above, per sequence ("DeepSeek MoE：从v1到v3的演进"
+// §DeepSeek-v3, sequence-wise balance loss).  Sequence q covers tokens
+// [cu[q], cu[q+1]) (clamped to [0, T], so any input stays in bounds); it is
+// cut into chunks of kSeqChunk tokens, each chunk summed by one workgroup
+// (fp64, token order), the chunks of a sequence reduced in order.
+constexpr int kSeqChunk = 64;
+
+size_t seq_stats_ws_bytes(int T, int N, int n_seq) {
+  const size_t chunks = static_cast<size_t>((T + kSeqChunk - 1) / kSeqChunk) + n_seq;
+  const size_t a = ((static_cast<size_t>(n_seq) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+  const size_t b = (chunks * N * sizeof(double) + 255) & ~size_t(255);
+  return a + b + chunks * N * sizeof(int32_t) + 256;
+}
+
+__device__ __forceinline__ int clamp_tok(int v, int T) { return v < 0 ? 0 : (v > T ? T : v); }
+
+// chunk_start[q] = chunks of the sequences before q; chunk_start[n_seq] = total
+__global__ __launch_bounds__(256) void seq_chunks_kernel(const int32_t* __restrict__ cu, int n_seq,
+                                                         int T, int32_t* __restrict__ chunk_start) {
+  __shared__ int sh[256];
+  int running = 0;
+  for (int q0 = 0; q0 < n_seq; q0 += 256) {
+    const int q = q0 + threadIdx.x;
+    int c = 0;
+    if (q < n_seq) {
+      const int a = clamp_tok(cu[q], T), b = clamp_tok(cu[q + 1], T);
+      c = b > a ? (b - a + kSeqChunk - 1) / kSeqChunk : 0;
+    }
+    sh[threadIdx.x] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = threadIdx.x >= o ? sh[threadIdx.x - o] : 0;
+      __syncthreads();
+      sh[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (q < n_seq) chunk_start[q] = running + sh[threadIdx.x] - c;
+    running += sh[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) chunk_start[n_seq] = running;
+}
+
+__global__ __launch_bounds__(256) void seq_partial_kernel(
+    const int32_t* __restrict__ cu, int n_seq, int T, int N, int k, int score_fn,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ logits, const float* __restrict__ lse, double* __restrict__ part,
+    int32_t* __restrict__ pcnt) {
+  __shared__ int hist[256];
+  const int b = blockIdx.x;
+  if (b >= chunk_start[n_seq]) return;  // uniform
+  // the last sequence whose first chunk is <= b owns chunk b
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_start[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int a = clamp_tok(cu[lo], T), e_end = clamp_tok(cu[lo + 1], T);
+  const int t0 = a + (b - chunk_start[lo]) * kSeqChunk;
+  const int t1 = min(e_end, t0 + kSeqChunk);
+  for (int e = threadIdx.x; e < N; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < (t1 - t0) * k; i += blockDim.x) {
+    const int e = topk_idx[static_cast<int64_t>(t0) * k + i];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicAdd(&hist[e], 1);  // integer
+  }
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    double acc = 0.0;
+    for (int t = t0; t < t1; ++t) {
+      const float l = logits[static_cast<int64_t>(t) * N + e];
+      const float sc = score_fn == MOE_SCORE_SIGMOID ? sigmoid_score(l) : __expf(l - lse[t]);
+      acc += static_cast<double>(sc);
+    }
+    part[static_cast<int64_t>(b) * N + e] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) pcnt[static_cast<int64_t>(b) * N + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void seq_final_kernel(
+    const int32_t* __restrict__ cu, int n_seq, int T, int N, int k, int max_chunks,
+    const int32_t* __restrict__ chunk_start, const double* __restrict__ part,
+    const int32_t* __restrict__ pcnt, float* __restrict__ f_seq, float* __restrict__ P_seq,
+    float* __restrict__ L_seq) {
+  __shared__ double sh[4];
+  const int q = blockIdx.x;
+  const int e = threadIdx.x;
+  const int Tq = max(0, clamp_tok(cu[q + 1], T) - clamp_tok(cu[q], T));
+  double col = 0.0;
+  long long cnt = 0;
+  // chunk ids beyond the partials written (only for overlapping, invalid
+  // boundaries) are not read
+  const int c_end = min(chunk_start[q + 1], max_chunks);
+  if (e < N)
+    for (int c = chunk_start[q]; c < c_end; ++c) {
+      col += part[static_cast<int64_t>(c) * N + e];
+      cnt += pcnt[static_cast<int64_t>(c) * N + e];
+    }
+  const double tot = block_sum_f64(col, sh);
+  const double fe = (e < N && Tq > 0 && k > 0) ? static_cast<double>(cnt) / (static_cast<double>(k) * Tq) : 0.0;
+  const double pe = (e < N && tot > 0.0) ? col / tot : 0.0;
+  const double lb = block_sum_f64(fe * pe, sh);
+  if (e < N) {
+    f_seq[static_cast<int64_t>(q) * N + e] = static_cast<float>(fe);
+    P_seq[static_cast<int64_t>(q) * N + e] = static_cast<float>(pe);
+  }
+  if (e == 0) L_seq[q] = static_cast<float>(N * lb);
+}
+
+// mean of L_seq over the non-empty sequences (0 when there are none)
+__global__ __launch_bounds__(256) void seq_mean_kernel(const int32_t* __restrict__ cu, int n_seq,
+                                                       int T, const float* __restrict__ L_seq,
+                                                       float* __restrict__ L_mean) {
+  __shared__ double sh[4];
+  double sum = 0.0, cnt = 0.0;
+  for (int q = threadIdx.x; q < n_seq; q += blockDim.x)
+    if (clamp_tok(cu[q + 1], T) > clamp_tok(cu[q], T)) {
+      sum += L_seq[q];
+      cnt += 1.0;
+    }
+  sum = block_sum_f64(sum, sh);
+  cnt = block_sum_f64(cnt, sh);
+  if (threadIdx.x == 0) L_mean[0] = cnt > 0.0 ? static_cast<float>(sum / cnt) : 0.f;
+}
+
+hipError_t launch_seq_stats(const int32_t* cu, int n_seq, const int32_t* topk_idx,
+                            const float* lse, const float* logits, int T, int N, int k,
+                            int score_fn, float* f_seq, float* P_seq, float* L_seq,
+                            float* L_mean, void* ws, hipStream_t st) {
+  const int chunks = (T + kSeqChunk - 1) / kSeqChunk + n_seq;
+  char* p = static_cast<char*>(ws);
+  int32_t* chunk_start = reinterpret_cast<int32_t*>(p);
+  p += ((static_cast<size_t>(n_seq) + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+  double* part = reinterpret_cast<double*>(p);
+  p += (static_cast<size_t>(chunks) * N * sizeof(double) + 255) & ~size_t(255);
+  int32_t* pcnt = reinterpret_cast<int32_t*>(p);
+  if (n_seq > 0) {
+    seq_chunks_kernel<<<1, 256, 0, st>>>(cu, n_seq, T, chunk_start);
+    if (chunks > 0)
+      seq_partial_kernel<<<chunks, 256, 0, st>>>(cu, n_seq, T, N, k, score_fn, chunk_start,
+                                                 topk_idx, logits, lse, part, pcnt);
+    seq_final_kernel<<<n_seq, 256, 0, st>>>(cu, n_seq, T, N, k, chunks, chunk_start, part, pcnt,
+                                            f_seq, P_seq, L_seq);
+  }
+  if (L_mean) seq_mean_kernel<<<1, 256, 0, st>>>(cu, n_seq, T, L_seq, L_mean);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- device-level stats
+// "DeepSeek MoE：从v1到v3的演进" §DeepSeek-v1, device-level balance loss: the
+// expert statistics summed over each of G groups of consecutive experts
+// (one group per device); L_dev = G sum_g F_g P_g.
+__global__ __launch_bounds__(256) void group_stats_kernel(const float* __restrict__ f,
+                                                          const float* __restrict__ P, int N,
+                                                          int G, float* __restrict__ F_g,
+                                                          float* __restrict__ P_g,
+                                                          float* __restrict__ L_dev) {
+  __shared__ double sh[4];
+  const int g = threadIdx.x;
+  const int gs = N / G;
+  double a = 0.0, b = 0.0;
+  if (g < G)
+    for (int e = g * gs; e < (g + 1) * gs; ++e) {
+      a += f[e];
+      b += P[e];
+    }
+  if (g < G) {
+    if (F_g) F_g[g] = static_cast<float>(a);
+    if (P_g) P_g[g] = static_cast<float>(b);
+  }
+  const double l = block_sum_f64(g < G ? a * b : 0.0, sh);
+  if (g == 0 && L_dev) L_dev[0] = static_cast<float>(G * l);
+}
+
+hipError_t launch_group_stats(const float* f, const float* P, int N, int G, float* F_g,
+                              float* P_g, float* L_dev, hipStream_t st) {
+  group_stats_kernel<<<1, 256, 0, st>>>(f, P, N, G, F_g, P_g, L_dev);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- bias
 // b_e += u * sign(mean(c) - c_e); the sign is taken exactly in integers as
 // sign(sum(c) - N c_e).

@@ -331,6 +331,41 @@ moe_status moe_load_stats(const moe_cfg* cfg, const int32_t* counts, const float
                                  f, P, scalars, ws, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_seq_load_stats_workspace_size(const moe_cfg* cfg, int32_t n_seq, size_t* bytes) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if (!bytes || n_seq < 0) return MOE_ERR_INVALID_ARG;
+  *bytes = seq_stats_ws_bytes(cfg->T, cfg->N, n_seq);
+  return MOE_OK;
+}
+
+moe_status moe_seq_load_stats(const moe_cfg* cfg, int32_t n_seq, const int32_t* cu_seqlens,
+                              const int32_t* topk_idx, const float* token_lse,
+                              const float* logits, float* f_seq, float* P_seq, float* L_seq,
+                              float* L_mean, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if (n_seq < 0) return MOE_ERR_INVALID_ARG;
+  if (n_seq > 0) {
+    if (!cu_seqlens || !f_seq || !P_seq || !L_seq) return MOE_ERR_INVALID_ARG;
+    if (cfg->T > 0 && (!logits || (cfg->k > 0 && !topk_idx))) return MOE_ERR_INVALID_ARG;
+    if (cfg->T > 0 && cfg->score_fn == MOE_SCORE_SOFTMAX && !token_lse) return MOE_ERR_INVALID_ARG;
+  }
+  if (!ws || ws_bytes < seq_stats_ws_bytes(cfg->T, cfg->N, n_seq)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_seq_stats(cu_seqlens, n_seq, topk_idx, token_lse, logits, cfg->T,
+                                     cfg->N, cfg->k, cfg->score_fn, f_seq, P_seq, L_seq, L_mean,
+                                     ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_group_load_stats(const moe_cfg* cfg, const float* f, const float* P,
+                                float* F_group, float* P_group, float* L_dev, void* stream) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if (!f || !P) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_group_stats(f, P, cfg->N, cfg->n_groups, F_group, P_group, L_dev,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_bias_update(const moe_cfg* cfg, const int32_t* counts, float* bias, float u,
                            void* stream) {
   moe_status s = check_cfg(cfg);

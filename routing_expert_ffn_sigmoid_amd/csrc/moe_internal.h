@@ -186,6 +186,13 @@ size_t stats_ws_bytes(int T, int N);
 hipError_t launch_stats(const int32_t* counts, const float* lse, const float* logits, int T,
                         int N, int k, int score_fn, float* f, float* P, float* scalars,
                         void* ws, hipStream_t st);
+size_t seq_stats_ws_bytes(int T, int N, int n_seq);
+hipError_t launch_seq_stats(const int32_t* cu, int n_seq, const int32_t* topk_idx,
+                            const float* lse, const float* logits, int T, int N, int k,
+                            int score_fn, float* f_seq, float* P_seq, float* L_seq,
+                            float* L_mean, void* ws, hipStream_t st);
+hipError_t launch_group_stats(const float* f, const float* P, int N, int G, float* F_g,
+                              float* P_g, float* L_dev, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int N, float u,
                               hipStream_t st);
 

@@ -174,3 +174,43 @@ def check_outputs(wl, out, ref_rows, tokens):
 
 def make_inputs(wl, device="cuda"):
     return synth.make_inputs(wl, device=device)
+
+
+def route_only(wl, logits, bias=None):
+    """moe_route on given fp32 logits: (topk_idx, topk_gate, topk_score, token_lse) tensors."""
+    cfg = moe.make_cfg(wl)
+    T, k = wl.T, wl.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    score = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T,), dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, None, None, logits.clone(), bias, idx, gate, score, lse)
+    torch.cuda.synchronize()
+    return idx, gate, score, lse
+
+
+def seq_stats_gpu(wl, cu, idx, lse, logits):
+    cfg = moe.make_cfg(wl)
+    S = len(cu) - 1
+    dev = "cuda"
+    f = torch.full((S, wl.N), float("nan"), dtype=torch.float32, device=dev)
+    P = torch.full((S, wl.N), float("nan"), dtype=torch.float32, device=dev)
+    L = torch.full((S,), float("nan"), dtype=torch.float32, device=dev)
+    Lm = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_seq_load_stats_workspace_size(cfg, S), dtype=torch.uint8, device=dev)
+    ws.fill_(0xCD)
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+    moe.moe_seq_load_stats(cfg, cu_t, idx, lse, logits, f, P, L, Lm, ws)
+    torch.cuda.synchronize()
+    return f.cpu().numpy(), P.cpu().numpy(), L.cpu().numpy(), float(Lm.cpu().numpy()[0])
+
+
+def check_seq_stats(wl, cu, idx, lse, logits):
+    f, P, L, Lm = seq_stats_gpu(wl, cu, idx, lse, logits)
+    ref = oracle.seq_load_stats(logits.cpu().numpy(), idx.cpu().numpy(), cu, wl.k,
+                                score_fn_const(wl))
+    for name, got, want in (("f", f, ref["f"]), ("P", P, ref["P"]), ("L", L, ref["L"])):
+        mr, _ = normwise(got, want)
+        assert mr <= F32_MAXREL, f"sequence {name} max-rel {mr}"
+    assert abs(Lm - ref["L_mean"]) <= F32_MAXREL * max(1.0, abs(ref["L_mean"]))
+    return ref

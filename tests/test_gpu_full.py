@@ -9,7 +9,8 @@ import torch
 import oracle
 from routing_expert_ffn_sigmoid_amd import workloads
 
-from gpu_common import (F32_MAXREL, check_dispatch, check_outputs, check_routing, check_stats,
+from gpu_common import (F32_MAXREL, check_dispatch, check_outputs, check_routing, check_seq_stats,
+                        check_stats,
                         f64, gpu, layer_forward, make_inputs, normwise, oracle_rows,
                         require_gpu, say, typed)
 
@@ -75,7 +76,11 @@ def test_v3_prefill_layer(v3_weights):
     from routing_expert_ffn_sigmoid_amd import synth
     inp = dict(v3_weights)
     inp["x"] = synth.normal((wl.T, wl.H), wl.x_std, torch.bfloat16, "cuda", wl.seed, f"x_T{wl.T}")
-    _run(wl, inp, 6)
+    _, aux, _ = _run(wl, inp, 6)
+    # the batch as four sequences of 2048 tokens (sequence-wise statistics)
+    ref = check_seq_stats(wl, [0, 2048, 4096, 6144, 8192], aux["topk_idx"], aux["token_lse"],
+                          aux["logits"])
+    say(f"  sequence-wise L_B {np.round(ref['L'], 4).tolist()} mean {ref['L_mean']:.4f}")
 
 
 def test_v3_decode_layer(v3_weights):
