@@ -342,11 +342,31 @@ def main():
     achieved_tflops = work["gate_up_flop"] / (gate_up_ms / 1e3) / 1e12
     kernel_src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")
     traffic = load_traffic(kernel_src, args.workload)
-    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": "ffn_bf16_kernel (SwiGLU gate/up, routed + shared)",
-                "per_launch_flop": work["gate_up_flop"], "avg_launch_ms": round(gate_up_ms, 4)}
+    # algorithmic bytes of the gate/up launch: the touched experts' gate/up
+    # weights, the shared expert's, x once, h written once
+    es = 2 if wl.act_dtype == 1 else 4
+    wsz = 2 if wl.w_dtype == 1 else 4
+    Ish = wl.n_shared * wl.I_shared
+    gate_up_bytes = (touched * 2 * wl.I * wl.H * wsz + 2 * Ish * wl.H * wsz + wl.T * wl.H * es
+                     + (kept * wl.I + wl.T * Ish) * es)
+    achieved_gbs = gate_up_bytes / (gate_up_ms / 1e3) / 1e9
+    mfma_roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
+                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    hbm_roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    # primary roof: HBM when the launch is clearly memory-bound (flop per
+    # algorithmic byte under half the ridge point 2500 TFLOP/s / 8 TB/s),
+    # MFMA otherwise; the other roof is reported beside it
+    intensity = work["gate_up_flop"] / gate_up_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    primary, secondary = (hbm_roof, mfma_roof) if intensity < 0.5 * ridge else (mfma_roof, hbm_roof)
+    roofline = dict(primary)
+    roofline.update({"traffic": traffic,
+                     "kernel": "ffn gate/up grouped GEMM (SwiGLU, routed + shared)",
+                     "per_launch_flop": work["gate_up_flop"], "per_launch_bytes": gate_up_bytes,
+                     "flop_per_byte": round(intensity, 1), "avg_launch_ms": round(gate_up_ms, 4),
+                     "beside": secondary})
     layer_tflops = work["layer_flop"] / (ms_per_step / 1e3) / 1e12
     touched_bytes = touched * 3 * wl.I * wl.H * 2 + 3 * wl.n_shared * wl.I_shared * wl.H * 2
 
