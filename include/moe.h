@@ -58,6 +58,18 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Layout of the expert weight matrices (w13, w2, ws13, ws2).  Each matrix
+ * is R rows (output features) by K columns (input features).
+ *   MOE_LAYOUT_ROWS:  row-major, element (r, c) at r*K + c.  fp32 weights.
+ *   MOE_LAYOUT_TILED: blocks of 16 rows x 32 columns (1 KiB in bf16); the
+ *     block of rows [16i, 16i+16) and columns [32j, 32j+32) starts at element
+ *     (i*(K/32) + j)*512, and inside it the 16-byte chunk number l (0..63)
+ *     holds row 16i + l%16, columns 32j + 8*(l/16) .. +7.  bf16 weights; R a
+ *     multiple of 16, K of 32.  Same size as row-major; moe_pack_weights
+ *     converts.  (Each chunk is one lane's MFMA fragment, so the kernels load
+ *     weights as contiguous KiBs.) */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
+
 /* Score function.  SIGMOID: s = 1/(1+e^-l), each expert independent
  * ([EVO] §DeepSeek-v3).  SOFTMAX: s = softmax over the N logits ([EVO]
  * §ST-MoE p_i(x); §DeepSeek-v1/v2 gate). */
@@ -87,10 +99,12 @@ typedef struct {
                            * lowest-scored ones; 0 = off, -1 = the average
                            * group load ceil(T*k / n_groups).  Exclusive with
                            * `capacity`.                                        */
+  int32_t w_layout;    /* moe_layout of the expert weights: MOE_LAYOUT_TILED for
+                        * bf16, MOE_LAYOUT_ROWS for fp32 (else UNSUPPORTED)  */
 } moe_cfg;
 
-/* Layer weights (device pointers):
- *   w_router [N, H]              router_dtype
+/* Layer weights (device pointers); the expert matrices in cfg->w_layout:
+ *   w_router [N, H]              router_dtype, row-major
  *   w13      [N, 2*I, H]         per expert: rows [0,I) gate, rows [I,2I) up
  *   w2       [N, H, I]           per expert: down projection
  *   ws13     [2*n_shared*I_shared, H]  the shared experts packed as one of
@@ -145,6 +159,16 @@ typedef struct {
   float* scalars;
   void** stage_events;
 } moe_aux;
+
+/* Convert n_mat row-major matrices of rows x cols (consecutive in src) to
+ * MOE_LAYOUT_TILED in dst: a one-time step when weights are loaded.
+ * dtype must be MOE_BF16 (else MOE_ERR_UNSUPPORTED), rows a multiple of 16
+ * and cols of 32 (else MOE_ERR_UNSUPPORTED); src and dst are device buffers
+ * of n_mat*rows*cols elements that must not overlap (MOE_ERR_INVALID_ARG).
+ * Example: w13 of a layer is n_mat = N, rows = 2*I, cols = H; w2 is N, H, I;
+ * ws13 is 1, 2*n_shared*I_shared, H; ws2 is 1, H, n_shared*I_shared. */
+moe_status moe_pack_weights(int64_t n_mat, int32_t rows, int32_t cols, int32_t dtype,
+                            const void* src, void* dst, void* stream);
 
 /* Bytes of workspace moe_layer_forward needs for cfg; also enough for any
  * single granular call below with the same cfg.  Returns MOE_ERR_INVALID_ARG

@@ -20,12 +20,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 STAGES = ["router_gemm", "route", "dispatch", "ffn_gate_up", "ffn_down", "combine", "stats"]
 N_STAGES = len(STAGES)
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_load_stats",
            "moe_seq_load_stats", "moe_seq_load_stats_workspace_size", "moe_group_load_stats",
+           "moe_pack_weights",
            "moe_bias_update", "moe_layer_forward", "moe_status_string"]
 
 _vp = ctypes.c_void_p
@@ -44,7 +47,7 @@ class MoeCfg(ctypes.Structure):
                 ("score_fn", _i32), ("norm_topk", _i32), ("route_scale", ctypes.c_float),
                 ("capacity", _i32), ("I", _i32), ("n_shared", _i32), ("I_shared", _i32),
                 ("act_dtype", _i32), ("w_dtype", _i32), ("router_dtype", _i32),
-                ("group_capacity", _i32)]
+                ("group_capacity", _i32), ("w_layout", _i32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -95,6 +98,8 @@ def lib():
         L.moe_seq_load_stats_workspace_size.argtypes = [cfgp, _i32, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_group_load_stats.restype = st
         L.moe_group_load_stats.argtypes = [cfgp] + [_vp] * 5 + [_vp]
+        L.moe_pack_weights.restype = st
+        L.moe_pack_weights.argtypes = [ctypes.c_int64, _i32, _i32, _i32, _vp, _vp, _vp]
         L.moe_bias_update.restype = st
         L.moe_bias_update.argtypes = [cfgp, _vp, _vp, ctypes.c_float, _vp]
         L.moe_layer_forward.restype = st
@@ -259,6 +264,31 @@ def moe_load_stats(cfg: MoeCfg, counts, token_lse, logits, f, P, scalars, ws, st
         _ptr(P, torch.float32, "P", (N,)), _ptr(scalars, torch.float32, "scalars", (3,)),
         wsp, wsb, _stream(stream))
     _check(code, "moe_load_stats")
+
+
+def pack_weights(w, stream=None):
+    """Row-major bf16 expert weights [..., R, K] -> a new tensor of the same
+    shape holding them in MOE_LAYOUT_TILED (moe_pack_weights)."""
+    torch = _torch()
+    if w.dtype != torch.bfloat16 or w.dim() < 2 or not w.is_contiguous():
+        raise ValueError("pack_weights: contiguous bf16 tensor [..., R, K] expected")
+    R, K = int(w.shape[-2]), int(w.shape[-1])
+    n_mat = w.numel() // (R * K) if R * K else 0
+    out = torch.empty_like(w)
+    _check(lib().moe_pack_weights(n_mat, R, K, MOE_BF16, _vp(w.data_ptr()), _vp(out.data_ptr()),
+                                  _stream(stream)), "moe_pack_weights")
+    return out
+
+
+def prepare_weights(cfg: MoeCfg, weights: dict, stream=None) -> dict:
+    """The layer weights as the library reads them: the expert matrices
+    (w13, w2, ws13, ws2) packed when cfg.w_layout is MOE_LAYOUT_TILED."""
+    out = dict(weights)
+    if cfg.w_layout == MOE_LAYOUT_TILED:
+        for n in ("w13", "w2", "ws13", "ws2"):
+            if out.get(n) is not None:
+                out[n] = pack_weights(out[n], stream)
+    return out
 
 
 def moe_seq_load_stats_workspace_size(cfg: MoeCfg, n_seq: int) -> int:

@@ -7,6 +7,10 @@
 // "从零构建DeepSeekMoE…" §2.2 (layer output = shared experts + routed
 // experts).  The expert form is SwiGLU: h = silu(Wg a) * (Wu a), y = Wd h.
 //
+// bf16 weights are tiled (see kTileElems): every wave-wide weight load is one
+// contiguous KiB that already holds each lane's MFMA fragment, which streams
+// from HBM measurably faster than 16 rows x 64 bytes of a row-major matrix.
+//
 // bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //  * workgroup = 4 waves; a wave computes all BM rows of the tile times 64
 //    weight rows (4 blocks of 16).  In the gate/up phase a wave's blocks are
@@ -49,6 +53,10 @@ namespace moe {
 #endif
 
 constexpr int kBK = 64;        // k per pipeline step (8 chunks of 16 bytes)
+// Tiled weights: blocks of 16 rows x 32 k (1 KiB, kTileElems elements); the
+// blocks of one 16-row group are consecutive in k, and inside a block lane
+// l's MFMA fragment (row l % 16, k 8 * (l / 16) .. + 7) is the l-th 16 bytes.
+constexpr int kTileElems = 512;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kMaxSegs = 1024; // flat segments over all groups per launch
 
@@ -161,21 +169,22 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__
     aoff[p] = r * kBK + ((ch ^ ((r >> 1) & 7)) * 8);
   }
 
-  // weight rows of this wave: 4 blocks of 16
+  // weight blocks of this wave: 4 tiled blocks of 16 rows; lane l's fragment
+  // of k-block kb is the 16 bytes at block + kb * 1 KiB + l * 16
   const bf16_t* W = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(c.s) * g.w_stride;
   const bf16_t* bptr[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    int brow;
+    int brow;  // first weight row of the block (blocks past n_out read block 0)
     if (SWIGLU) {
-      const int col = c.nt * 128 + wave * 32 + (nb & 1) * 16 + (lane & 15);
+      const int col = c.nt * 128 + wave * 32 + (nb & 1) * 16;
       const int cc = col < g.n_out ? col : 0;
       brow = (nb < 2) ? cc : g.up_off + cc;
     } else {
-      const int col = c.nt * 256 + wave * 64 + nb * 16 + (lane & 15);
+      const int col = c.nt * 256 + wave * 64 + nb * 16;
       brow = col < g.n_out ? col : 0;
     }
-    bptr[nb] = W + static_cast<int64_t>(brow) * K + (lane >> 4) * 8;
+    bptr[nb] = W + static_cast<int64_t>(brow) * K + lane * 8;
   }
 
   f32x4 acc[NMB][4];
@@ -192,7 +201,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        dst[ks][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + step * kBK + ks * 32);
+        dst[ks][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + (step * 2 + ks) * kTileElems);
   };
   auto load_a = [&](int step) {
 #pragma unroll
@@ -435,11 +444,13 @@ __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
   for (int ks = 0; ks < 2; ++ks) {
     const int ch = (ks * 4 + (lane >> 4)) ^ swz;
     const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK + ch * 8;
-    const bf16_t* bbase = Bb + (lane & 15) * kBK + ch * 8;
+    // weight LDS slots: row block q, k-block ks at slot 2q + ks, fragment order
+    const bf16_t* bbase = Bb + ks * kTileElems + lane * 8;
     bf16x8 bf[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
-      bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK));
+      bf[nb] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 2 * kTileElems));
     bf16x8 af[NMBW];
 #pragma unroll
     for (int j = 0; j < kReadAhead && j < NMBW; ++j)
@@ -535,24 +546,27 @@ __device__ __noinline__ void big_tile(const FfnGroup& g, int s, int nt, int mrow
     if (g.row_index) prow = g.row_index[prow];
     aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
   }
-  // weight rows: tile row r = p*64 + 8*wave + lane/8
+  // weights, tiled: a step (64 k) of the tile is 16 row blocks x 2 k-blocks
+  // of 1 KiB; instruction j = p*8 + wave copies block (j / 2, k-block j % 2)
+  // into LDS slot j as is (fragment order)
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
   const int col0 = SWIGLU ? nt * 128 : nt * 256;
-  const uint32_t boff =
-      static_cast<uint32_t>(col0 + wave * 8 + (lane >> 3)) * krow_bytes + logical * 16;
+  const uint32_t boff = static_cast<uint32_t>(wave & 1) * 1024u + lane * 16u;
   auto b_soff = [&](int p) -> uint32_t {
-    // tile rows p*64..; in the gate/up phase rows 128.. are the up half
-    if (SWIGLU && p >= 2) return static_cast<uint32_t>(g.up_off + (p - 2) * 64) * krow_bytes;
-    return static_cast<uint32_t>(p * 64) * krow_bytes;
+    const int q = 4 * p + (wave >> 1);  // row block of the tile
+    // gate/up phase: blocks 8.. are the up half
+    if (SWIGLU && q >= 8) return static_cast<uint32_t>(g.up_off + col0 + 16 * (q - 8)) * krow_bytes;
+    return static_cast<uint32_t>(col0 + 16 * q) * krow_bytes;
   };
 
   auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
     const uint32_t kb = static_cast<uint32_t>(step) * (kBK * 2);
+    const uint32_t kw = static_cast<uint32_t>(step) * 2048u;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int q = p * 8 + wave;
       if (q * 8 < rows_needed) dma16(ra, aoff[p], kb, Ab + q * 8 * kBK);
-      dma16(rb, boff, b_soff(p) + kb, Bb + q * 8 * kBK);
+      dma16(rb, boff, b_soff(p) + kw, Bb + q * kTileElems);
     }
   };
 
@@ -677,10 +691,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   }
 }
 
-#ifndef MOE_FFN_L2_PREFETCH
-#define MOE_FFN_L2_PREFETCH 0
-#endif
-
 template <int NMBW, bool SWIGLU>
 __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
                                              const bf16_t* __restrict__ Bb, f32x4 (&acc)[8][4],
@@ -690,11 +700,11 @@ __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
   // ((lane%16) >> 1) & 3: one base per operand, block offsets are immediates
   const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
   const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
-  const bf16_t* bbase = Bb + (lane & 15) * kBK4 + ch * 8;
+  const bf16_t* bbase = Bb + lane * 8;  // weight slots are in fragment order
   bf16x8 bf[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * 16 * kBK4));
+    bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * kTileElems));
   bf16x8 af[NMBW];
 #pragma unroll
   for (int j = 0; j < kReadAhead && j < NMBW; ++j)
@@ -714,8 +724,7 @@ __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
 template <int NMBW, bool SWIGLU>
 __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
                                        bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
-                                       bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3,
-                                       bf16_t* scratch) {
+                                       bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -743,10 +752,12 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
     if (g.row_index) prow = g.row_index[prow];
     aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
   }
+  // weights, tiled: the wave copies the KiB of k-block `step` of row blocks
+  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
+  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
   const int col0 = SWIGLU ? nt * 128 : nt * 256;
-  const uint32_t boff =
-      static_cast<uint32_t>(col0 + wave * 16 + (lane >> 2)) * krow_bytes + logical * 16;
+  const uint32_t boff = static_cast<uint32_t>(col0 + wave * 16) * krow_bytes + lane * 16u;
   const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
   const bool a0 = (0 * 8 + wave) * 16 < rows_needed;
   const bool a1 = (1 * 8 + wave) * 16 < rows_needed;
@@ -760,38 +771,11 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
     const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
     if (a0) dma16(ra, aoff[0], kb, Ab + (0 * 8 + wave) * 16 * kBK4);
     if (a1) dma16(ra, aoff[1], kb, Ab + (1 * 8 + wave) * 16 * kBK4);
-    dma16(rb, boff, kb, Bb + (0 * 8 + wave) * 16 * kBK4);
-    dma16(rb, boff, bsoff1 + kb, Bb + (1 * 8 + wave) * 16 * kBK4);
+    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
+    dma16(rb, boff, kw, Bb + (0 * 8 + wave) * kTileElems);
+    dma16(rb, boff, bsoff1 + kw, Bb + (1 * 8 + wave) * kTileElems);
     cnt += 2 + (a0 ? 1 : 0) + (a1 ? 1 : 0);
   };
-#if MOE_FFN_L2_PREFETCH > 0
-  // L2 warm-up of stages still further ahead: one 16-byte request per
-  // 128-byte line (two k-steps of 32), one wave instruction per 64 rows;
-  // waves 0-3 cover the 256 activation rows, waves 4-7 the 256 weight rows.
-  // The bytes land in a wave-private scratch slot of LDS and are never read.
-  uint32_t pf_off;
-  {
-    const int r = (wave & 3) * 64 + lane;
-    if (wave < 4) {
-      int prow = mrow0 + min(r, mv - 1);
-      if (g.row_index) prow = g.row_index[prow];
-      pf_off = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u;
-    } else {
-      const int brow = SWIGLU ? (r < 128 ? col0 + r : g.up_off + col0 + (r - 128)) : col0 + r;
-      pf_off = static_cast<uint32_t>(brow) * krow_bytes;
-    }
-  }
-  const bool pf_active = wave < 4 ? ((wave & 3) * 64 < rows_needed) : true;
-  auto prefetch = [&](int step) {  // lines of steps (step, step+1), step even
-    if (step < nk && pf_active) {
-      dma16(wave < 4 ? ra : rb, pf_off, static_cast<uint32_t>(step) * (kBK4 * 2),
-            scratch + wave * 512);
-      ++cnt;
-    }
-  };
-#else
-  auto prefetch = [&](int) {};
-#endif
   auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
 
   f32x4 acc[8][4];
@@ -806,14 +790,12 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
   mark[1] = cnt;
   issue(2, A2, B2);
   mark[2] = cnt;
-  constexpr int PD = MOE_FFN_L2_PREFETCH;  // stages beyond the loads in flight
   for (int st = 0; st < nk; st += kStages) {
     // step st (buffer 0)
     wait_stage(0);
     __builtin_amdgcn_s_barrier();
     if (st + 3 < nk) issue(st + 3, A3, B3);
     mark[3] = cnt;
-    if (PD > 0) prefetch(st + 3 + PD + ((3 + PD) & 1));
     big4_compute<NMBW, SWIGLU>(A0, B0, acc, wm, wn);
     // step st+1 (buffer 1)
     wait_stage(1);
@@ -826,7 +808,6 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
     __builtin_amdgcn_s_barrier();
     if (st + 5 < nk) issue(st + 5, A1, B1);
     mark[1] = cnt;
-    if (PD > 0) prefetch(st + 5 + PD + ((5 + PD) & 1));
     big4_compute<NMBW, SWIGLU>(A2, B2, acc, wm, wn);
     // step st+3 (buffer 3)
     wait_stage(3);
@@ -848,7 +829,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
   __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t Pf[8 * 512];  // L2 warm-up landing slots
   __shared__ int tstart[kMaxSegs + 1];
   __shared__ int tmp[kThreads];
 
@@ -884,239 +864,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
     switch (nmbw) {
-      case 8: big4_tile<8, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 7: big4_tile<7, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 6: big4_tile<6, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 5: big4_tile<5, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 4: big4_tile<4, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 3: big4_tile<3, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      case 2: big4_tile<2, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-      default: big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3, Pf); break;
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------
-// Weight-streaming variant for large segments.  Only the activation tile is
-// staged in LDS (kAStages stages of 32 k, kAStages-1 in flight); each of the
-// 8 waves owns two 16-row weight blocks of the 256-wide tile (gate/up phase:
-// the gate and the up block of the same 16 h-columns) and streams them from
-// memory straight into registers kBPF steps ahead.  Every wave computes all
-// tile rows, so a short tile shortens every wave's work.
-// ---------------------------------------------------------------------
-#ifndef MOE_FFN_A_STAGES
-#define MOE_FFN_A_STAGES 6
-#endif
-#ifndef MOE_FFN_B_PF
-#define MOE_FFN_B_PF 5
-#endif
-constexpr int kAStages = MOE_FFN_A_STAGES;
-constexpr int kBPF = MOE_FFN_B_PF;
-
-constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
-
-template <int NMB, bool SWIGLU>
-__device__ __noinline__ void big5_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                       bf16_t* As) {
-  constexpr int BUF = 256 * kBK4;  // elements per activation stage
-  constexpr int NSLOT = kBPF + 1;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int K = wave_uniform(g.K);
-  const int nk = K / kBK4;
-
-  // activation DMA: 16 rows x 64 bytes per wave instruction, row group
-  // q = p*8 + wave (p = 0, 1) covers rows [16q, 16q+16); lane -> row
-  // 16q + lane/4, physical chunk lane%4, logical chunk
-  // (lane%4) ^ ((row >> 1) & 3) = (lane%4) ^ ((lane >> 3) & 3)
-  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const int rows_needed = NMB * 16;
-  uint32_t aoff[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int row = (p * 8 + wave) * 16 + (lane >> 2);
-    int prow = mrow0 + min(row, mv - 1);
-    if (g.row_index) prow = g.row_index[prow];
-    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
-  }
-  const bool a0 = (0 * 8 + wave) * 16 < rows_needed;
-  const bool a1 = (1 * 8 + wave) * 16 < rows_needed;
-
-  // weight fragments of this wave: block nb (0, 1), lane -> row lane%16,
-  // k-chunk lane/16 of each 32-wide step
-  const bf16_t* W = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride;
-  const bf16_t* bptr[2];
-  int col[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    int c, brow;
-    if (SWIGLU) {
-      c = nt * 128 + wave * 16 + (lane & 15);
-      const int cc = c < g.n_out ? c : g.n_out - 1;
-      brow = nb == 0 ? cc : g.up_off + cc;
-    } else {
-      c = nt * 256 + wave * 32 + nb * 16 + (lane & 15);
-      brow = c < g.n_out ? c : g.n_out - 1;
-    }
-    col[nb] = c;
-    bptr[nb] = W + static_cast<int64_t>(brow) * K + (lane >> 4) * 8;
-  }
-
-  int cnt = 0;              // vector-memory instructions issued by this wave
-  int mark[kAStages] = {};  // cnt after each activation stage's loads
-  auto issue_a = [&](int step, int buf) {
-    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
-    bf16_t* Ab = As + buf * BUF;
-    if (a0) dma16(ra, aoff[0], kb, Ab + (0 * 8 + wave) * 16 * kBK4);
-    if (a1) dma16(ra, aoff[1], kb, Ab + (1 * 8 + wave) * 16 * kBK4);
-    cnt += (a0 ? 1 : 0) + (a1 ? 1 : 0);
-  };
-  u32x4 bbuf[NSLOT][2];
-  auto issue_b = [&](int step, u32x4 (&dst)[2]) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      dst[nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + step * kBK4);
-    cnt += 2;
-  };
-
-  f32x4 acc[NMB][2];
-#pragma unroll
-  for (int j = 0; j < NMB; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
-  auto compute = [&](int buf, const u32x4 (&b)[2]) {
-    const bf16_t* abase = As + buf * BUF + (lane & 15) * kBK4 + ch * 8;
-    const bf16x8 b0 = as_bf16x8(b[0]);
-    const bf16x8 b1 = as_bf16x8(b[1]);
-#pragma unroll
-    for (int j = 0; j < NMB; ++j) {
-      const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 16 * kBK4));
-      acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, af, acc[j][0], 0, 0, 0);
-      acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, af, acc[j][1], 0, 0, 0);
-    }
-  };
-
-  // prologue: weights for steps 0..kBPF-1, activations for stages 0..S-2
-#pragma unroll
-  for (int u = 0; u < kBPF; ++u)
-    if (u < nk) issue_b(u, bbuf[u]);
-#pragma unroll
-  for (int u = 0; u < kAStages - 1; ++u) {
-    if (u < nk) issue_a(u, u);
-    mark[u] = cnt;
-  }
-  // main loop: the activation buffer index advances mod kAStages and the
-  // weight slot mod NSLOT; both are static inside an unrolled block of
-  // lcm(kAStages, NSLOT) steps
-  constexpr int UNR = kAStages * NSLOT / gcd_c(kAStages, NSLOT);
-  for (int s0 = 0; s0 < nk; s0 += UNR) {
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int st = s0 + u;
-      if (st < nk) {
-        const int abuf = u % kAStages;
-        wait_vmcnt_dyn(cnt - mark[abuf]);
-        __builtin_amdgcn_s_barrier();
-        if (st + kAStages - 1 < nk) issue_a(st + kAStages - 1, (u + kAStages - 1) % kAStages);
-        mark[(u + kAStages - 1) % kAStages] = cnt;
-        if (st + kBPF < nk) issue_b(st + kBPF, bbuf[(u + kBPF) % NSLOT]);
-        compute(abuf, bbuf[u % NSLOT]);
-      }
-    }
-  }
-
-  // epilogue: rows mrow0 + 16j + lane%16, 4 consecutive columns per lane
-  bf16_t* Out = static_cast<bf16_t*>(g.Out);
-  const int rl = lane & 15;
-  const int cq = (lane >> 4) * 4;
-#pragma unroll
-  for (int j = 0; j < NMB; ++j) {
-    const int r = j * 16 + rl;
-    if (r < mv) {
-      bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
-      if (SWIGLU) {
-        const int cc = nt * 128 + wave * 16 + cq;
-        if (cc < g.n_out) {
-          uint32_t w[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float g0 = acc[j][0][2 * h], g1 = acc[j][0][2 * h + 1];
-            const float u0 = acc[j][1][2 * h], u1 = acc[j][1][2 * h + 1];
-            const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
-            const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-            w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
-          }
-          *reinterpret_cast<u32x2*>(orow + cc) = u32x2{w[0], w[1]};
-        }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int cc = nt * 256 + wave * 32 + nb * 16 + cq;
-          if (cc < g.n_out) {
-            const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
-                                (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
-            const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
-                                (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
-            *reinterpret_cast<u32x2*>(orow + cc) = u32x2{w0, w1};
-          }
-        }
-      }
-    }
-  }
-  (void)col;
-}
-
-template <bool SWIGLU>
-__global__ __launch_bounds__(kBigThreads, 1) void ffn_big5_kernel(FfnLaunch a) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[kAStages * 256 * kBK4];
-  __shared__ int tstart[kMaxSegs + 1];
-  __shared__ int tmp[kThreads];
-
-  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
-  if (threadIdx.x < kThreads) build_tile_starts<kBigRows>(a, nsegT, tstart, tmp);
-  else build_tile_starts_idle();
-  const int total = tstart[nsegT];
-  const int nxcd = 8;
-  const int per = gridDim.x / nxcd;
-  const int xcd = blockIdx.x % nxcd;
-  const int slot = blockIdx.x / nxcd;
-  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
-  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
-
-  for (int L = lo + slot; L < hi; L += per) {
-    int i0 = 0, i1 = nsegT;
-    while (i1 - i0 > 1) {
-      const int mid = (i0 + i1) >> 1;
-      if (tstart[mid] <= L) i0 = mid;
-      else i1 = mid;
-    }
-    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
-    const FfnGroup g = grp ? a.g[1] : a.g[0];
-    const int s = grp ? i0 - a.g[0].nseg : i0;
-    const int r0 = seg_begin(g, s);
-    const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + kBigRows - 1) / kBigRows;
-    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
-    const int local = L - tstart[i0];
-    const int nt = local / mtc;
-    const int mt = local - nt * mtc;
-    const int mrow0 = r0 + mt * rpt;
-    const int mv = min(rpt, rows - mt * rpt);
-    const int nmb = (mv + 15) >> 4;
-    switch ((nmb + 1) >> 1) {  // live blocks rounded up to an even count
-      case 8: big5_tile<16, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 7: big5_tile<14, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 6: big5_tile<12, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 5: big5_tile<10, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 4: big5_tile<8, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 3: big5_tile<6, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      case 2: big5_tile<4, SWIGLU>(g, s, nt, mrow0, mv, As); break;
-      default: big5_tile<2, SWIGLU>(g, s, nt, mrow0, mv, As); break;
+      case 8: big4_tile<8, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 7: big4_tile<7, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 6: big4_tile<6, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 5: big4_tile<5, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 4: big4_tile<4, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 3: big4_tile<3, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      case 2: big4_tile<2, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+      default: big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
     }
     __syncthreads();
   }
@@ -1176,15 +931,6 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   // long-K gate/up phase (K = hidden), the 2-stage one on the down phase
   // (K = expert width, fewer k-steps per tile to amortise the deeper fill)
   k128 = k128 && phase == 0;
-#ifdef MOE_FFN_BIG5
-  if (fl.g[0].K % kBK4 == 0 && (fl.ngroups < 2 || fl.g[1].K % kBK4 == 0)) {
-    if (phase == 0)
-      ffn_big5_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
-    else
-      ffn_big5_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
-    return hipGetLastError();
-  }
-#endif
 #ifndef MOE_FFN_NO_BIG4
   if (k128) {
     if (phase == 0)
@@ -1219,6 +965,42 @@ hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int r
   if (rows_hint >= 128) return launch_mb<MOE_FFN_BIG_MB, MOE_FFN_BIG_PF>(fl, phase, MOE_FFN_MINBLK, st);
   if (rows_hint >= 32) return launch_mb<MOE_FFN_MID_MB, MOE_FFN_MID_PF>(fl, phase, 2, st);
   return launch_mb<1, MOE_FFN_SMALL_PF>(fl, phase, 2, st);
+}
+
+// ================================================================ weight packing
+// Row-major [n_mat][R][K] -> tiled: 16-row x 32-k blocks of 1 KiB, the blocks
+// of a 16-row group consecutive in k, inside a block lane l's fragment (row
+// l % 16, k-chunk l / 16 of 8 elements) at the l-th 16 bytes.  One 16-byte
+// chunk per thread and iteration.
+__global__ __launch_bounds__(256) void pack_tiled_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n_chunks,
+                                                         int R, int K) {
+  const int64_t kc = K / 8;       // 16-byte chunks per row
+  const int64_t kbn = K / 32;     // k-blocks per 16-row group
+  const int64_t per_mat = static_cast<int64_t>(R) * kc;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < n_chunks;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t mat = idx / per_mat;
+    const int64_t rem = idx - mat * per_mat;
+    const int64_t blk = rem / 64;
+    const int l = static_cast<int>(rem - blk * 64);
+    const int64_t rb = blk / kbn;
+    const int64_t kb = blk - rb * kbn;
+    const int64_t row = rb * 16 + (l & 15);
+    dst[idx] = src[mat * per_mat + row * kc + kb * 4 + (l >> 4)];
+  }
+}
+
+hipError_t launch_pack_tiled(const void* src, void* dst, int64_t n_mat, int R, int K,
+                             hipStream_t st) {
+  const int64_t n_chunks = n_mat * R * static_cast<int64_t>(K) / 8;
+  if (n_chunks <= 0) return hipSuccess;
+  int64_t blocks = (n_chunks + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  pack_tiled_kernel<<<static_cast<int>(blocks), 256, 0, st>>>(static_cast<const u32x4*>(src),
+                                                               static_cast<u32x4*>(dst), n_chunks,
+                                                               R, K);
+  return hipGetLastError();
 }
 
 // ================================================================ fp32 path

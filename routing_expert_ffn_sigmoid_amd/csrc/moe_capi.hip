@@ -36,9 +36,13 @@ moe_status check_cfg(const moe_cfg* c) {
   if (c->H % 64 != 0 || c->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && (static_cast<long long>(c->n_shared) * c->I_shared) % 64 != 0)
     return MOE_ERR_UNSUPPORTED;
+  if (c->w_layout != MOE_LAYOUT_ROWS && c->w_layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (c->group_capacity < -1) return MOE_ERR_INVALID_ARG;
   if (c->group_capacity != 0 && c->capacity > 0) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != c->w_dtype) return MOE_ERR_UNSUPPORTED;
+  // bf16 expert weights are read tiled, fp32 ones row-major
+  if (c->w_layout != (c->w_dtype == MOE_BF16 ? MOE_LAYOUT_TILED : MOE_LAYOUT_ROWS))
+    return MOE_ERR_UNSUPPORTED;
   // dropping keys hold the token index in 24 bits
   if ((c->capacity > 0 || c->group_capacity != 0) && c->T >= (1 << 24)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -329,6 +333,19 @@ moe_status moe_load_stats(const moe_cfg* cfg, const int32_t* counts, const float
   if (!ws || ws_bytes < stats_ws_bytes(cfg->T, cfg->N)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_stats(counts, token_lse, logits, cfg->T, cfg->N, cfg->k, cfg->score_fn,
                                  f, P, scalars, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_pack_weights(int64_t n_mat, int32_t rows, int32_t cols, int32_t dtype,
+                            const void* src, void* dst, void* stream) {
+  if (n_mat < 0 || rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows % 16 != 0 || cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  const uint64_t bytes = static_cast<uint64_t>(n_mat) * rows * cols * 2;
+  const uint64_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // overlapping
+  return hip_status(launch_pack_tiled(src, dst, n_mat, rows, cols, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_seq_load_stats_workspace_size(const moe_cfg* cfg, int32_t n_seq, size_t* bytes) {

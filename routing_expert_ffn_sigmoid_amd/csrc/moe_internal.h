@@ -186,6 +186,8 @@ size_t stats_ws_bytes(int T, int N);
 hipError_t launch_stats(const int32_t* counts, const float* lse, const float* logits, int T,
                         int N, int k, int score_fn, float* f, float* P, float* scalars,
                         void* ws, hipStream_t st);
+hipError_t launch_pack_tiled(const void* src, void* dst, int64_t n_mat, int R, int K,
+                             hipStream_t st);
 size_t seq_stats_ws_bytes(int T, int N, int n_seq);
 hipError_t launch_seq_stats(const int32_t* cu, int n_seq, const int32_t* topk_idx,
                             const float* lse, const float* logits, int T, int N, int k,

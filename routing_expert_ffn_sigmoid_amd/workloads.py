@@ -59,6 +59,11 @@ class Workload:
     def assignments(self) -> int:
         return self.T * self.k
 
+    @property
+    def w_layout(self) -> int:
+        """Expert weight layout the library reads: tiled for bf16, rows for fp32."""
+        return 1 if self.w_dtype == BF16 else 0
+
 
 def capacity_for(T: int, k: int, N: int, factor_num: int = 5, factor_den: int = 4) -> int:
     """Per-expert capacity ceil(factor * T * k / N) in integer arithmetic

@@ -68,7 +68,7 @@ def layer_forward(wl, inp, ws=None, aux=None, cfg=None):
         aux = moe.alloc_aux(cfg)
     if ws is None:
         ws = moe.alloc_workspace(cfg)
-    weights = {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")}
+    weights = moe.prepare_weights(cfg, {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")})
     moe.moe_layer_forward(cfg, weights, inp["x"], inp["bias"], out, aux, ws)
     torch.cuda.synchronize()
     return out, aux

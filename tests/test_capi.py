@@ -75,6 +75,8 @@ def test_workspace_size_for_presets(name):
     ({"N": 16, "n_groups": 8, "topk_groups": 2}, moe.MOE_ERR_UNSUPPORTED),  # groups of 2
     ({"w_dtype": 1}, moe.MOE_ERR_UNSUPPORTED),
     ({"group_capacity": -2}, moe.MOE_ERR_INVALID_ARG),
+    ({"w_layout": 5}, moe.MOE_ERR_INVALID_ARG),
+    ({"w_layout": 1}, moe.MOE_ERR_UNSUPPORTED),           # fp32 weights are read row-major
     ({"group_capacity": -1, "capacity": 4}, moe.MOE_ERR_INVALID_ARG),  # one policy at a time
     ({"T": 1 << 24, "capacity": 4}, moe.MOE_ERR_UNSUPPORTED),  # 24-bit token field of the keys
     ({"T": 1 << 24, "group_capacity": -1}, moe.MOE_ERR_UNSUPPORTED),
@@ -119,3 +121,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_LIB", None)
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+@needs_lib
+def test_bf16_weights_must_be_tiled():
+    cfg = moe.make_cfg(workloads.V1)
+    assert cfg.w_layout == moe.MOE_LAYOUT_TILED
+    assert _ws_size(cfg)[0] == moe.MOE_OK
+    cfg.w_layout = moe.MOE_LAYOUT_ROWS
+    assert _ws_size(cfg)[0] == moe.MOE_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_pack_weights_argument_checks():
+    L = moe.lib()
+    fake = ctypes.c_void_p(0x10000)
+    other = ctypes.c_void_p(0x10000 + 3 * 32 * 64 * 2)
+    assert L.moe_pack_weights(3, 32, 64, moe.MOE_F32, fake, other, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(3, 24, 64, moe.MOE_BF16, fake, other, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(3, 32, 48, moe.MOE_BF16, fake, other, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(-1, 32, 64, moe.MOE_BF16, fake, other, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(3, 32, 64, moe.MOE_BF16, None, other, None) == moe.MOE_ERR_INVALID_ARG
+    # overlapping source and destination
+    near = ctypes.c_void_p(0x10000 + 1024)
+    assert L.moe_pack_weights(3, 32, 64, moe.MOE_BF16, fake, near, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(3, 32, 64, moe.MOE_BF16, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    # nothing to do
+    assert L.moe_pack_weights(0, 32, 64, moe.MOE_BF16, None, None, None) == moe.MOE_OK

@@ -193,7 +193,8 @@ def test_grouped_ffn_ragged_segments(rows_per_seg):
     y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(moe.moe_grouped_ffn_workspace_size(cfg, M, inter), dtype=torch.uint8,
                      device="cuda")
-    moe.moe_grouped_ffn(cfg, nseg, torch.from_numpy(offs).cuda(), M, inter, a, None, w13, w2,
+    moe.moe_grouped_ffn(cfg, nseg, torch.from_numpy(offs).cuda(), M, inter, a, None,
+                        moe.pack_weights(w13), moe.pack_weights(w2),
                         y, ws)
     torch.cuda.synchronize()
     ref = np.empty((M, H))
@@ -285,3 +286,23 @@ def test_granular_calls_compose_to_layer_forward():
     torch.cuda.synchronize()
     mr, _ = normwise(f64(out), f64(out_ref))
     assert mr <= F32_MAXREL
+
+
+@pytest.mark.parametrize("shape", [(3, 48, 96), (1, 16, 32), (2, 4096, 7168)])
+def test_pack_weights_layout(shape):
+    """moe_pack_weights against the tiled layout written out element by
+    element: block (i, j) of 16 rows x 32 columns at (i*(K/32) + j)*512,
+    chunk l of the block = row 16i + l%16, columns 32j + 8(l/16) .. +7."""
+    require_gpu()
+    n, R, K = shape
+    say(f"pack {shape}")
+    w = torch.arange(n * R * K, device="cuda", dtype=torch.int32).reshape(n, R, K)
+    w = (w % 65521).to(torch.int16).view(torch.bfloat16)  # distinct-ish bit patterns
+    p = moe.pack_weights(w)
+    torch.cuda.synchronize()
+    src = w.view(torch.int16).cpu().numpy()
+    got = p.view(torch.int16).cpu().numpy().reshape(n, R * K)
+    # reference built with numpy index arithmetic
+    blk = src.reshape(n, R // 16, 16, K // 32, 4, 8)        # mat, i, row-in-block, j, chunk, e
+    ref = blk.transpose(0, 1, 3, 4, 2, 5).reshape(n, R * K)  # mat, i, j, chunk, row, e
+    np.testing.assert_array_equal(got, ref)
