@@ -468,8 +468,8 @@ __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
   }
 }
 
-template <bool SWIGLU>
-__device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&acc)[8][4],
+template <int NJ, bool SWIGLU>
+__device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
                                              int nmbw, int wm, int wn, int nt, int mrow0,
                                              int mv) {
   const int lane = threadIdx.x & 63;
@@ -477,7 +477,7 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
   const int rl = lane & 15;
   const int cq = (lane >> 4) * 4;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     if (j < nmbw) {
       const int r = (2 * j + wm) * 16 + rl;
       if (r < mv) {
@@ -593,7 +593,7 @@ __device__ __noinline__ void big_tile(const FfnGroup& g, int s, int nt, int mrow
     big_compute<NMBW, SWIGLU>(As0, Bs0, acc, wm, wn);
     __syncthreads();
   }
-  big_epilogue<SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+  big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
 }
 
 template <bool SWIGLU>
@@ -660,7 +660,19 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // ---------------------------------------------------------------------
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
-constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB per operand stage
+constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
+// Activation rows per tile of the 4-stage kernel (a multiple of 32, at most
+// 384).  Taller tiles keep an expert slightly over 256 rows in one tile, but
+// on the V3-shaped prefill layer 320 measured 2 % slower than 256 (fewer,
+// less even tiles per CU; the two halves of a split expert already share its
+// weights through L2).
+#ifndef MOE_FFN_BIG4_ROWS
+#define MOE_FFN_BIG4_ROWS 256
+#endif
+constexpr int kBig4Rows = MOE_FFN_BIG4_ROWS;
+static_assert(kBig4Rows % 32 == 0 && kBig4Rows <= 384, "tile rows");
+constexpr int kBig4MaxNmbw = kBig4Rows / 32;
+constexpr int kBuf4AElems = kBig4Rows * kBK4;
 
 // s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
 template <int N>
@@ -687,14 +699,14 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     case 12: wait_vmcnt<12>(); break;
     case 13: wait_vmcnt<13>(); break;
     case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 3 stages x 4 + 3
+    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 2 stages x 5 loads
   }
 }
 
 template <int NMBW, bool SWIGLU>
 __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
-                                             const bf16_t* __restrict__ Bb, f32x4 (&acc)[8][4],
-                                             int wm, int wn) {
+                                             const bf16_t* __restrict__ Bb,
+                                             f32x4 (&acc)[NMBW][4], int wm, int wn) {
   const int lane = threadIdx.x & 63;
   // fragment row = 16*block + lane%16; swizzle term ((row >> 1) & 3) is
   // ((lane%16) >> 1) & 3: one base per operand, block offsets are immediates
@@ -744,13 +756,16 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(
       static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
   const int rows_needed = (2 * NMBW) * 16;
-  uint32_t aoff[2];
+  constexpr int NAG = (2 * NMBW + 7) / 8;  // activation row groups of 16 per wave (at most)
+  uint32_t aoff[NAG];
+  bool aact[NAG];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < NAG; ++p) {
     const int row = (p * 8 + wave) * 16 + (lane >> 2);
     int prow = mrow0 + min(row, mv - 1);
     if (g.row_index) prow = g.row_index[prow];
     aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+    aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
   }
   // weights, tiled: the wave copies the KiB of k-block `step` of row blocks
   // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
@@ -759,8 +774,6 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
   const int col0 = SWIGLU ? nt * 128 : nt * 256;
   const uint32_t boff = static_cast<uint32_t>(col0 + wave * 16) * krow_bytes + lane * 16u;
   const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
-  const bool a0 = (0 * 8 + wave) * 16 < rows_needed;
-  const bool a1 = (1 * 8 + wave) * 16 < rows_needed;
 
   // Every vector-memory instruction this wave issues in the tile is counted
   // (cnt); mark[b] is cnt right after stage b's loads.  Waiting for stage b
@@ -769,18 +782,22 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
   int mark[kStages] = {0, 0, 0, 0};
   auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
     const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
-    if (a0) dma16(ra, aoff[0], kb, Ab + (0 * 8 + wave) * 16 * kBK4);
-    if (a1) dma16(ra, aoff[1], kb, Ab + (1 * 8 + wave) * 16 * kBK4);
+#pragma unroll
+    for (int p = 0; p < NAG; ++p)
+      if (aact[p]) {
+        dma16(ra, aoff[p], kb, Ab + (p * 8 + wave) * 16 * kBK4);
+        ++cnt;
+      }
     const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
     dma16(rb, boff, kw, Bb + (0 * 8 + wave) * kTileElems);
     dma16(rb, boff, bsoff1 + kw, Bb + (1 * 8 + wave) * kTileElems);
-    cnt += 2 + (a0 ? 1 : 0) + (a1 ? 1 : 0);
+    cnt += 2;
   };
   auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
 
-  f32x4 acc[8][4];
+  f32x4 acc[NMBW][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NMBW; ++j)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -816,15 +833,15 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
     mark[2] = cnt;
     big4_compute<NMBW, SWIGLU>(A3, B3, acc, wm, wn);
   }
-  big_epilogue<SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+  big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
 }
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
-  __shared__ __attribute__((aligned(16))) bf16_t A0[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t A1[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t A2[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t A3[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t A0[kBuf4AElems];
+  __shared__ __attribute__((aligned(16))) bf16_t A1[kBuf4AElems];
+  __shared__ __attribute__((aligned(16))) bf16_t A2[kBuf4AElems];
+  __shared__ __attribute__((aligned(16))) bf16_t A3[kBuf4AElems];
   __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
@@ -833,7 +850,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
   __shared__ int tmp[kThreads];
 
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
-  if (threadIdx.x < kThreads) build_tile_starts<kBigRows>(a, nsegT, tstart, tmp);
+  if (threadIdx.x < kThreads) build_tile_starts<kBig4Rows>(a, nsegT, tstart, tmp);
   else build_tile_starts_idle();
   const int total = tstart[nsegT];
   const int nxcd = 8;
@@ -855,7 +872,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int s = grp ? i0 - a.g[0].nseg : i0;
     const int r0 = seg_begin(g, s);
     const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + kBigRows - 1) / kBigRows;
+    const int mtc = (rows + kBig4Rows - 1) / kBig4Rows;
     const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
     const int local = L - tstart[i0];
     const int nt = local / mtc;
@@ -864,6 +881,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
     switch (nmbw) {
+#if MOE_FFN_BIG4_ROWS > 352
+      case 12: big4_tile<12, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+#endif
+#if MOE_FFN_BIG4_ROWS > 320
+      case 11: big4_tile<11, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+#endif
+#if MOE_FFN_BIG4_ROWS > 288
+      case 10: big4_tile<10, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+#endif
+#if MOE_FFN_BIG4_ROWS > 256
+      case 9: big4_tile<9, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
+#endif
       case 8: big4_tile<8, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
       case 7: big4_tile<7, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
       case 6: big4_tile<6, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
