@@ -22,10 +22,13 @@
 //    memory straight into registers, PF steps ahead.
 //  * M-blocks of 16 rows past the end of a segment are skipped, so a
 //    segment's last tile costs what its rows need (to 16 rows).
-//  * persistent grid: each XCD (workgroup id mod 8) walks a contiguous eighth
-//    of the tile list, so tiles that share an expert's weights (consecutive
-//    m-tiles of one n-tile) and its activations (consecutive n-tiles) meet in
-//    that XCD's L2.
+//  * persistent grid, XCD-aware (workgroup id mod 8 is its XCD): tiles that
+//    share an expert's weights (consecutive m-tiles of one n-tile) and its
+//    activations (consecutive n-tiles) are handed to the same XCD at the same
+//    time, so they meet in that XCD's L2.  The large-segment kernels deal the
+//    tile list out in rounds (each XCD a run of consecutive tiles per round),
+//    which keeps the XCDs equally loaded; the small-segment kernel gives each
+//    XCD a contiguous eighth of the list.
 #include "moe_internal.h"
 
 namespace moe {
@@ -48,6 +51,9 @@ namespace moe {
 #define MOE_FFN_SMALL_PF 4
 #endif
 
+#ifndef MOE_FFN_SMALL_BPC
+#define MOE_FFN_SMALL_BPC 2  // workgroups per CU of the small-segment launch
+#endif
 #ifndef MOE_FFN_MINBLK
 #define MOE_FFN_MINBLK 2
 #endif
@@ -613,10 +619,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
   const int per = gridDim.x / nxcd;
   const int xcd = blockIdx.x % nxcd;
   const int slot = blockIdx.x / nxcd;
-  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
-  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
-
-  for (int L = lo + slot; L < hi; L += per) {
+  // rounds of gridDim.x consecutive tiles; inside a round XCD x takes the
+  // x-th run of `per` tiles (two experts' n-tiles: shared activation rows in
+  // one L2), and every XCD gets work in every round
+  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
     int i0 = 0, i1 = nsegT;
     while (i1 - i0 > 1) {
       const int mid = (i0 + i1) >> 1;
@@ -857,10 +863,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
   const int per = gridDim.x / nxcd;
   const int xcd = blockIdx.x % nxcd;
   const int slot = blockIdx.x / nxcd;
-  const int lo = static_cast<int>((static_cast<int64_t>(total) * xcd) / nxcd);
-  const int hi = static_cast<int>((static_cast<int64_t>(total) * (xcd + 1)) / nxcd);
-
-  for (int L = lo + slot; L < hi; L += per) {
+  // rounds of gridDim.x consecutive tiles; inside a round XCD x takes the
+  // x-th run of `per` tiles (two experts' n-tiles: shared activation rows in
+  // one L2), and every XCD gets work in every round
+  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
     int i0 = 0, i1 = nsegT;
     while (i1 - i0 > 1) {
       const int mid = (i0 + i1) >> 1;
@@ -993,7 +999,7 @@ hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int r
 #endif
   if (rows_hint >= 128) return launch_mb<MOE_FFN_BIG_MB, MOE_FFN_BIG_PF>(fl, phase, MOE_FFN_MINBLK, st);
   if (rows_hint >= 32) return launch_mb<MOE_FFN_MID_MB, MOE_FFN_MID_PF>(fl, phase, 2, st);
-  return launch_mb<1, MOE_FFN_SMALL_PF>(fl, phase, 2, st);
+  return launch_mb<1, MOE_FFN_SMALL_PF>(fl, phase, MOE_FFN_SMALL_BPC, st);
 }
 
 // ================================================================ weight packing
