@@ -410,6 +410,35 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
                                            wave_uniform(soffset), 0, 0);
 }
 
+// s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 2 stages x 5 loads
+  }
+}
+
 constexpr int kBigThreads = 512;  // 8 waves, 2 per SIMD
 
 // Wave (wm, wn) = (wave & 1, wave >> 1): M-blocks 2j + wm (j < NMBW), four
@@ -523,85 +552,174 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
   }
 }
 
-// The k-loop of one tile with NMBW live M-blocks per wave.
-template <int NMBW, bool SWIGLU>
-__device__ __noinline__ void big_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                         bf16_t* As0, bf16_t* As1, bf16_t* Bs0, bf16_t* Bs1) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int K = wave_uniform(g.K);
-  const int nk = K / kBK;
+// Tiles run back to back: the first stage of the next tile is loaded during
+// the last step of the current one, before the current tile's stores, so the
+// next tile's first wait skips those stores (vmcnt retires in issue order)
+// and no tile starts with an empty pipeline.
+struct BigTile {
+  int grp, s, nt, mrow0, mv, nmbw, nk;
+};
 
-  // 4 DMA row groups per operand per thread: group q = p*8 + wave covers
-  // tile rows [8q, 8q+8); this lane brings row 8q + lane/8, physical chunk
-  // lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7), where
-  // (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.
+// Where a tile's operands come from (plain values; buffer descriptors are
+// built from them at issue time).
+struct BigLoads {
+  const void* a_base;
+  const void* w_base;
+  uint32_t a_bytes, w_bytes;
+  uint32_t aoff[4];   // per lane: activation row byte offset + chunk
+  uint32_t bsoff[4];  // uniform: first weight row of each row-block pair, in bytes
+  int rows_needed;
+};
+
+__device__ __forceinline__ BigTile big_decode(const FfnLaunch& a, const int* tstart, int nsegT,
+                                              int L) {
+  int i0 = 0, i1 = nsegT;
+  while (i1 - i0 > 1) {
+    const int mid = (i0 + i1) >> 1;
+    if (tstart[mid] <= L) i0 = mid;
+    else i1 = mid;
+  }
+  BigTile t;
+  t.grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+  const FfnGroup g = t.grp ? a.g[1] : a.g[0];
+  t.s = t.grp ? i0 - a.g[0].nseg : i0;
+  const int r0 = seg_begin(g, t.s);
+  const int rows = seg_end(g, t.s) - r0;
+  const int mtc = (rows + kBigRows - 1) / kBigRows;
+  const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
+  const int local = L - tstart[i0];
+  t.nt = local / mtc;
+  const int mt = local - t.nt * mtc;
+  t.mrow0 = r0 + mt * rpt;
+  t.mv = min(rpt, rows - mt * rpt);
+  t.nmbw = (((t.mv + 15) >> 4) + 1) >> 1;  // blocks per wave (interleaved)
+  t.nk = g.K / kBK;
+  return t;
+}
+
+// DMA geometry: 4 activation row groups per thread, group q = p*8 + wave
+// covers tile rows [8q, 8q+8); this lane brings row 8q + lane/8, physical
+// chunk lane%8, i.e. logical chunk (lane%8) ^ ((row >> 1) & 7), where
+// (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.  Weights, tiled: a
+// step (64 k) of the tile is 16 row blocks x 2 k-blocks of 1 KiB;
+// instruction j = p*8 + wave copies block (j / 2, k-block j % 2) into LDS
+// slot j as is (fragment order).
+template <bool SWIGLU>
+__device__ __forceinline__ BigLoads big_loads(const FfnGroup& g, const BigTile& t, int wave,
+                                              int lane) {
+  BigLoads L;
+  L.a_base = g.A;
+  L.a_bytes = g.a_bytes;
+  L.w_base = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(t.s) * g.w_stride;
+  L.w_bytes = g.w_bytes;
   const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
-  uint32_t aoff[4];
-  const int rows_needed = (2 * NMBW) * 16;  // tile rows any wave reads
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int row = (p * 8 + wave) * 8 + (lane >> 3);
-    int prow = mrow0 + min(row, mv - 1);
+    int prow = t.mrow0 + min(row, t.mv - 1);
     if (g.row_index) prow = g.row_index[prow];
-    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+    L.aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
   }
-  // weights, tiled: a step (64 k) of the tile is 16 row blocks x 2 k-blocks
-  // of 1 KiB; instruction j = p*8 + wave copies block (j / 2, k-block j % 2)
-  // into LDS slot j as is (fragment order)
-  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const int col0 = SWIGLU ? nt * 128 : nt * 256;
-  const uint32_t boff = static_cast<uint32_t>(wave & 1) * 1024u + lane * 16u;
-  auto b_soff = [&](int p) -> uint32_t {
-    const int q = 4 * p + (wave >> 1);  // row block of the tile
-    // gate/up phase: blocks 8.. are the up half
-    if (SWIGLU && q >= 8) return static_cast<uint32_t>(g.up_off + col0 + 16 * (q - 8)) * krow_bytes;
-    return static_cast<uint32_t>(col0 + 16 * q) * krow_bytes;
-  };
-
-  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
-    const uint32_t kb = static_cast<uint32_t>(step) * (kBK * 2);
-    const uint32_t kw = static_cast<uint32_t>(step) * 2048u;
+  const uint32_t krow_bytes = static_cast<uint32_t>(g.K) * 2u;
+  const int col0 = SWIGLU ? t.nt * 128 : t.nt * 256;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int q = p * 8 + wave;
-      if (q * 8 < rows_needed) dma16(ra, aoff[p], kb, Ab + q * 8 * kBK);
-      dma16(rb, boff, b_soff(p) + kw, Bb + q * kTileElems);
-    }
-  };
-
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  issue(0, As0, Bs0);
-  __syncthreads();
-  // two steps per iteration (buffer 0 then 1); no accumulator update sits
-  // under a condition inside the loop
-  int st = 0;
-  for (; st + 1 < nk; st += 2) {
-    issue(st + 1, As1, Bs1);
-    big_compute<NMBW, SWIGLU>(As0, Bs0, acc, wm, wn);
-    __syncthreads();
-    if (st + 2 < nk) issue(st + 2, As0, Bs0);
-    big_compute<NMBW, SWIGLU>(As1, Bs1, acc, wm, wn);
-    __syncthreads();
+  for (int p = 0; p < 4; ++p) {
+    const int q = 4 * p + (wave >> 1);  // row block of the tile; gate/up: 8.. are the up half
+    const int wr = (SWIGLU && q >= 8) ? g.up_off + col0 + 16 * (q - 8) : col0 + 16 * q;
+    L.bsoff[p] = wave_uniform(static_cast<uint32_t>(wr) * krow_bytes);
   }
-  if (st < nk) {  // odd step count: the last step sits in buffer 0
-    big_compute<NMBW, SWIGLU>(As0, Bs0, acc, wm, wn);
-    __syncthreads();
-  }
-  big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+  L.rows_needed = 2 * t.nmbw * 16;  // tile rows any wave reads
+  return L;
 }
 
+__device__ __forceinline__ void big_issue(const BigLoads& L, int step, bf16_t* Ab, bf16_t* Bb,
+                                          int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(wave_uniform(L.a_base), L.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(wave_uniform(L.w_base), L.w_bytes);
+  const uint32_t kb = static_cast<uint32_t>(step) * (kBK * 2);
+  const uint32_t kw = static_cast<uint32_t>(step) * 2048u;
+  const uint32_t boff = static_cast<uint32_t>(wave & 1) * 1024u + lane * 16u;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int q = p * 8 + wave;
+    if (q * 8 < L.rows_needed) dma16(ra, L.aoff[p], kb, Ab + q * 8 * kBK);
+    dma16(rb, boff, L.bsoff[p] + kw, Bb + q * kTileElems);
+  }
+}
+
+// s_waitcnt vmcnt(n) for the store counts a 2-stage tile epilogue issues
+__device__ __forceinline__ void wait_vmcnt_upto32(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 28: wait_vmcnt<28>(); break;
+    case 32: wait_vmcnt<32>(); break;
+    default: wait_vmcnt<0>(); break;  // waiting for more is always correct
+  }
+}
+
+// Stores of a finished tile: one 8-byte buffer store per (M-block, column
+// block) and lane, issued unconditionally (a lane outside the tile gets an
+// offset past the buffer bound, which the hardware drops), so the count is
+// fixed: NMBW * (SWIGLU ? 2 : 4).
+template <int NMBW, bool SWIGLU>
+__device__ __forceinline__ int big_store(const FfnGroup& g, const f32x4 (&acc)[8][4], int wm,
+                                         int wn, int nt, int mrow0, int mv) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(wave_uniform(static_cast<const void*>(g.Out)), g.o_bytes);
+  const int rl = lane & 15;
+  const int cq = (lane >> 4) * 4;
+  const uint32_t ldo2 = static_cast<uint32_t>(g.ldo) * 2u;
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j) {
+    const int r = (2 * j + wm) * 16 + rl;
+    const bool rv = r < mv;
+    const uint32_t rowoff = static_cast<uint32_t>(mrow0 + r) * ldo2;
+    if (SWIGLU) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = nt * 128 + wn * 32 + nb * 16 + cq;
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float g0 = acc[j][nb][2 * h], g1 = acc[j][nb][2 * h + 1];
+          const float u0 = acc[j][nb + 2][2 * h], u1 = acc[j][nb + 2][2 * h + 1];
+          const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+          const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+          w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+        }
+        const uint32_t off = (rv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, ro, off, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = nt * 256 + wn * 64 + nb * 16 + cq;
+        const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
+        const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
+        const uint32_t off = (rv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off, 0, 0);
+      }
+    }
+  }
+  return NMBW * (SWIGLU ? 2 : 4);
+}
+
+// Persistent loop of the 2-stage kernel.  Every tile runs the 8-M-block
+// compute (a short tile's extra MFMAs read rows that are never stored),
+// while loads and stores cover only the tile's rows; one instantiation keeps
+// the whole loop, both tiles' load addresses included, in registers.
 template <bool SWIGLU>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
   __shared__ __attribute__((aligned(16))) bf16_t As0[kBigBufElems];
@@ -619,40 +737,55 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
   const int per = gridDim.x / nxcd;
   const int xcd = blockIdx.x % nxcd;
   const int slot = blockIdx.x / nxcd;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
   // rounds of gridDim.x consecutive tiles; inside a round XCD x takes the
   // x-th run of `per` tiles (two experts' n-tiles: shared activation rows in
   // one L2), and every XCD gets work in every round
-  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
-    int i0 = 0, i1 = nsegT;
-    while (i1 - i0 > 1) {
-      const int mid = (i0 + i1) >> 1;
-      if (tstart[mid] <= L) i0 = mid;
-      else i1 = mid;
+  int L = xcd * per + slot;
+  if (L >= total) return;  // whole workgroup
+  BigTile t = big_decode(a, tstart, nsegT, L);
+  BigLoads cur = big_loads<SWIGLU>(t.grp ? a.g[1] : a.g[0], t, wave, lane);
+  big_issue(cur, 0, As0, Bs0, wave, lane);
+  int par = 0;        // buffer of the tile's first step
+  int pending = 0;    // store instructions issued after the current step's loads
+  for (;;) {
+    const int Ln = L + static_cast<int>(gridDim.x);
+    const bool has_next = Ln < total;
+    BigTile tn = t;
+    BigLoads nxt = cur;
+    if (has_next) {
+      tn = big_decode(a, tstart, nsegT, Ln);
+      nxt = big_loads<SWIGLU>(tn.grp ? a.g[1] : a.g[0], tn, wave, lane);
     }
-    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
-    const FfnGroup g = grp ? a.g[1] : a.g[0];
-    const int s = grp ? i0 - a.g[0].nseg : i0;
-    const int r0 = seg_begin(g, s);
-    const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + kBigRows - 1) / kBigRows;
-    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
-    const int local = L - tstart[i0];
-    const int nt = local / mtc;
-    const int mt = local - nt * mtc;
-    const int mrow0 = r0 + mt * rpt;
-    const int mv = min(rpt, rows - mt * rpt);
-    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;  // blocks per wave (interleaved)
-    switch (nmbw) {
-      case 8: big_tile<8, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 7: big_tile<7, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 6: big_tile<6, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 5: big_tile<5, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 4: big_tile<4, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 3: big_tile<3, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      case 2: big_tile<2, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
-      default: big_tile<1, SWIGLU>(g, s, nt, mrow0, mv, As0, As1, Bs0, Bs1); break;
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < t.nk; ++st) {
+      const int b = (par + st) & 1;
+      // this wave's loads of step st have landed (the previous tile's
+      // stores, issued after them, may still be in flight at st == 0);
+      // after the barrier every wave's share is in LDS and the other buffer
+      // is no longer read
+      if (st == 0) wait_vmcnt_upto32(pending);
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      bf16_t* Ac = b ? As1 : As0;
+      bf16_t* Bc = b ? Bs1 : Bs0;
+      if (st + 1 < t.nk) big_issue(cur, st + 1, b ? As0 : As1, b ? Bs0 : Bs1, wave, lane);
+      else if (has_next) big_issue(nxt, 0, b ? As0 : As1, b ? Bs0 : Bs1, wave, lane);
+      big_compute<8, SWIGLU>(Ac, Bc, acc, wm, wn);
     }
-    __syncthreads();
+    pending = big_store<8, SWIGLU>(t.grp ? a.g[1] : a.g[0], acc, wm, wn, t.nt, t.mrow0, t.mv);
+    if (!has_next) break;
+    par = (par + t.nk) & 1;
+    L = Ln;
+    t = tn;
+    cur = nxt;
   }
 }
 
@@ -680,34 +813,6 @@ static_assert(kBig4Rows % 32 == 0 && kBig4Rows <= 384, "tile rows");
 constexpr int kBig4MaxNmbw = kBig4Rows / 32;
 constexpr int kBuf4AElems = kBig4Rows * kBK4;
 
-// s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 2 stages x 5 loads
-  }
-}
 
 template <int NMBW, bool SWIGLU>
 __device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
@@ -994,7 +1099,7 @@ hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int r
 #ifndef MOE_FFN_NO_BIG
   bool big_ok = true;  // buffer addressing needs 32-bit byte offsets
   for (int i = 0; i < ngroups; ++i)
-    big_ok = big_ok && groups[i].a_bytes != 0 && groups[i].w_bytes != 0;
+    big_ok = big_ok && groups[i].a_bytes != 0 && groups[i].w_bytes != 0 && groups[i].o_bytes != 0;
   if (rows_hint >= 128 && big_ok) return launch_big(fl, phase, st);
 #endif
   if (rows_hint >= 128) return launch_mb<MOE_FFN_BIG_MB, MOE_FFN_BIG_PF>(fl, phase, MOE_FFN_MINBLK, st);

@@ -148,11 +148,13 @@ moe_status run_ffn(const moe_cfg* c, const void* x, const int32_t* row_token,
     a.rows = TK; a.W = w->w13; a.w_stride = 2LL * c->I * c->H; a.Out = h_r; a.ldo = c->I;
     a.K = c->H; a.n_out = c->I; a.up_off = c->I;
     a.a_bytes = bound32(c->T, c->H, es); a.w_bytes = bound32(2LL * c->I, c->H, es);
+    a.o_bytes = bound32(TK, c->I, es);
     FfnGroup b{};
     b.A = h_r; b.lda = c->I; b.row_index = nullptr; b.seg_off = offsets; b.nseg = c->N;
     b.rows = TK; b.W = w->w2; b.w_stride = static_cast<int64_t>(c->H) * c->I; b.Out = y_r;
     b.ldo = c->H; b.K = c->I; b.n_out = c->H; b.up_off = 0;
     b.a_bytes = bound32(TK, c->I, es); b.w_bytes = bound32(c->H, c->I, es);
+    b.o_bytes = bound32(TK, c->H, es);
     g0[n] = a;
     g1[n] = b;
     ++n;
@@ -163,11 +165,13 @@ moe_status run_ffn(const moe_cfg* c, const void* x, const int32_t* row_token,
     a.rows = c->T; a.W = w->ws13; a.w_stride = 0; a.Out = h_s; a.ldo = Ish;
     a.K = c->H; a.n_out = Ish; a.up_off = Ish;
     a.a_bytes = bound32(c->T, c->H, es); a.w_bytes = bound32(2LL * Ish, c->H, es);
+    a.o_bytes = bound32(c->T, Ish, es);
     FfnGroup b{};
     b.A = h_s; b.lda = Ish; b.row_index = nullptr; b.seg_off = nullptr; b.nseg = 1;
     b.rows = c->T; b.W = w->ws2; b.w_stride = 0; b.Out = y_s; b.ldo = c->H;
     b.K = Ish; b.n_out = c->H; b.up_off = 0;
     b.a_bytes = bound32(c->T, Ish, es); b.w_bytes = bound32(c->H, Ish, es);
+    b.o_bytes = bound32(c->T, c->H, es);
     g0[n] = a;
     g1[n] = b;
     ++n;
@@ -297,12 +301,14 @@ moe_status moe_grouped_ffn(const moe_cfg* cfg, int32_t n_segments, const int32_t
   // without that bound the buffer-addressed kernel is not used
   g0.a_bytes = row_index ? 0u : bound32(max_rows, cfg->H, esize(cfg->act_dtype));
   g0.w_bytes = bound32(2LL * inter, cfg->H, esize(cfg->act_dtype));
+  g0.o_bytes = bound32(max_rows, inter, esize(cfg->act_dtype));
   FfnGroup g1{};
   g1.A = ws; g1.lda = inter; g1.row_index = nullptr; g1.seg_off = seg_offsets;
   g1.nseg = n_segments; g1.rows = max_rows; g1.W = w2; g1.w_stride = static_cast<int64_t>(cfg->H) * inter;
   g1.Out = y; g1.ldo = cfg->H; g1.K = inter; g1.n_out = cfg->H; g1.up_off = 0;
   g1.a_bytes = bound32(max_rows, inter, esize(cfg->act_dtype));
   g1.w_bytes = bound32(cfg->H, inter, esize(cfg->act_dtype));
+  g1.o_bytes = bound32(max_rows, cfg->H, esize(cfg->act_dtype));
   if (cfg->act_dtype == MOE_BF16) {
     const int hint = max_rows / n_segments;
     MOE_TRY(launch_ffn_bf16(&g0, 1, 0, hint, st));

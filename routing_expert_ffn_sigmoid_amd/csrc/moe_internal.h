@@ -170,6 +170,7 @@ struct FfnGroup {
   int32_t up_off;           // gate/up phase: row offset of the up half (= inter)
   uint32_t a_bytes;         // bytes addressable from A (buffer bound; 0 = unknown)
   uint32_t w_bytes;         // bytes of one segment's weights (buffer bound; 0 = unknown)
+  uint32_t o_bytes;         // bytes addressable from Out (buffer bound; 0 = unknown)
 };
 // phase 0: gate/up + SwiGLU -> h;  phase 1: down projection -> y.
 // `rows_hint`: expected rows per segment (chooses the tile height).
