@@ -30,6 +30,7 @@
 //    which keeps the XCDs equally loaded; the small-segment kernel gives each
 //    XCD a contiguous eighth of the list.
 #include "moe_internal.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -374,49 +375,6 @@ constexpr int kBigRows = 256;   // max rows per tile
 constexpr int kBigCols = 256;   // weight rows per tile
 constexpr int kBigBufElems = 256 * kBK;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Values every lane of a wave holds equally, made visible to the compiler as
-// such (scalar registers): buffer descriptors and the LDS target of a direct
-// load must be wave-uniform, otherwise the compiler wraps the load in a
-// per-lane loop.
-__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
-}
-template <typename T>
-__device__ __forceinline__ T* wave_uniform(T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = wave_uniform(static_cast<uint32_t>(v));
-  const uint32_t hi = wave_uniform(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Raw buffer resource over [base, base + bytes) (gfx9 descriptor: no
-// swizzle, 32-bit data); loads past `bytes` return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform(base)), 0,
-                                           wave_uniform(bytes), 0x00020000);
-}
-
-// One wave moves 8 rows x 128 bytes of an operand tile straight into LDS:
-// lane -> 16 bytes at lds_group + 16 * lane (row lane/8, physical chunk
-// lane%8).  voffset already selects the logical chunk the XOR swizzle keeps
-// at that physical position.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
-                                      bf16_t* lds_group) {
-  // lds_group is derived from the wave index made uniform by the caller
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_group, 16, voffset,
-                                           wave_uniform(soffset), 0, 0);
-}
-
-// s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   switch (n) {
@@ -556,6 +514,25 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
 // the last step of the current one, before the current tile's stores, so the
 // next tile's first wait skips those stores (vmcnt retires in issue order)
 // and no tile starts with an empty pipeline.
+// Tile order inside one segment of mtc row tiles x ntc column tiles: row
+// tiles are taken in groups of up to kGroupM, and inside a group the order is
+// column-major (all row tiles of the group for column tile 0, then column 1,
+// ...).  A run of 32 consecutive tiles (one XCD's share of a round) then covers
+// a block of several row tiles by several column tiles, whose activation rows
+// and weight rows are each fetched once into that XCD's L2.  Segments of at
+// most kGroupM row tiles (every routed expert at the usual sizes) keep the
+// plain column-major order; the 8192-row shared segment of a prefill batch no
+// longer streams all of x once per column tile.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_nm(int local, int mtc, int ntc, int& nt, int& mt) {
+  const int g = local / (kGroupM * ntc);
+  const int m0 = g * kGroupM;
+  const int gm = min(kGroupM, mtc - m0);
+  const int w = local - g * kGroupM * ntc;
+  nt = w / gm;
+  mt = m0 + (w - nt * gm);
+}
+
 struct BigTile {
   int grp, s, nt, mrow0, mv, nmbw, nk;
 };
@@ -588,8 +565,8 @@ __device__ __forceinline__ BigTile big_decode(const FfnLaunch& a, const int* tst
   const int mtc = (rows + kBigRows - 1) / kBigRows;
   const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
   const int local = L - tstart[i0];
-  t.nt = local / mtc;
-  const int mt = local - t.nt * mtc;
+  int mt;
+  tile_nm(local, mtc, t.grp ? a.nt[1] : a.nt[0], t.nt, mt);
   t.mrow0 = r0 + mt * rpt;
   t.mv = min(rpt, rows - mt * rpt);
   t.nmbw = (((t.mv + 15) >> 4) + 1) >> 1;  // blocks per wave (interleaved)
@@ -986,8 +963,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int mtc = (rows + kBig4Rows - 1) / kBig4Rows;
     const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
     const int local = L - tstart[i0];
-    const int nt = local / mtc;
-    const int mt = local - nt * mtc;
+    int nt, mt;
+    tile_nm(local, mtc, grp ? a.nt[1] : a.nt[0], nt, mt);
     const int mrow0 = r0 + mt * rpt;
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;

@@ -64,9 +64,9 @@ DropPolicy drop_policy(const moe_cfg* c) {
 }
 
 struct LayerLayout {
-  size_t part, logits, idx, gate, score, lse, counts, offsets, ndrop, disp, row_token, inv_row;
+  size_t router, logits, idx, gate, score, lse, counts, offsets, ndrop, disp, row_token, inv_row;
   size_t h_r, h_s, y_r, y_s, stats, f, P, scalars, total;
-  int splits;
+  RouterPlan rp;
 };
 
 LayerLayout layout(const moe_cfg* c) {
@@ -80,8 +80,8 @@ LayerLayout layout(const moe_cfg* c) {
     o += a256(bytes > 0 ? bytes : 1);
     return at;
   };
-  L.splits = router_splits(c->T, c->H, c->N);
-  L.part = take(L.splits > 1 ? L.splits * T * N * 4 : 0);
+  L.rp = router_plan(c->T, c->H, c->N, c->act_dtype, c->router_dtype);
+  L.router = take(L.rp.ws_bytes);
   L.logits = take(T * N * 4);
   L.idx = take(TK * 4);
   L.gate = take(TK * 4);
@@ -225,16 +225,11 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router, fl
   const float* part = logits;
   int splits = 1;
   if (x) {
-    splits = router_splits(cfg->T, cfg->H, cfg->N);
-    float* dst = logits;
-    if (splits > 1) {
-      const size_t need = static_cast<size_t>(splits) * cfg->T * cfg->N * 4;
-      if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-      dst = static_cast<float*>(ws);
-      part = dst;
-    }
-    MOE_TRY(launch_router_gemm(x, cfg->act_dtype, w_router, cfg->router_dtype, dst, cfg->T,
-                               cfg->H, cfg->N, splits, st));
+    const RouterPlan rp = router_plan(cfg->T, cfg->H, cfg->N, cfg->act_dtype, cfg->router_dtype);
+    if (rp.ws_bytes > 0 && (!ws || ws_bytes < rp.ws_bytes)) return MOE_ERR_WORKSPACE;
+    splits = rp.splits;
+    MOE_TRY(launch_router_gemm(rp, x, cfg->act_dtype, w_router, cfg->router_dtype, logits, ws,
+                               cfg->T, cfg->H, cfg->N, &part, st));
   }
   RouteParams p{};
   p.part = part; p.splits = splits; p.logits = logits; p.bias = bias; p.topk_idx = topk_idx;
@@ -431,13 +426,13 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
 
   // 1. router GEMM
   record(aux, MOE_STAGE_ROUTER_GEMM, st);
-  float* part = L.splits > 1 ? at<float>(ws, L.part) : logits;
-  MOE_TRY(launch_router_gemm(x, cfg->act_dtype, w->w_router, cfg->router_dtype, part, T, cfg->H,
-                             N, L.splits, st));
+  const float* part = logits;
+  MOE_TRY(launch_router_gemm(L.rp, x, cfg->act_dtype, w->w_router, cfg->router_dtype, logits,
+                             at<char>(ws, L.router), T, cfg->H, N, &part, st));
   // 2. scores, group limit, top-k, gates
   record(aux, MOE_STAGE_ROUTE, st);
   RouteParams p{};
-  p.part = part; p.splits = L.splits; p.logits = logits; p.bias = bias; p.topk_idx = idx;
+  p.part = part; p.splits = L.rp.splits; p.logits = logits; p.bias = bias; p.topk_idx = idx;
   p.topk_gate = gate; p.topk_score = score; p.token_lse = lse; p.T = T; p.N = N; p.k = k;
   p.n_groups = cfg->n_groups; p.topk_groups = cfg->topk_groups; p.group_topn = cfg->group_topn;
   p.score_fn = cfg->score_fn; p.norm_topk = cfg->norm_topk; p.route_scale = cfg->route_scale;

@@ -105,10 +105,31 @@ __device__ __forceinline__ float sigmoid_score(float l) {
 // ------------------------------------------------------------------ launchers
 // Every launcher enqueues on `st` and returns hipGetLastError().
 
-// logits partials: part[s][t][e] = sum over split s of x[t,h] * wg[e,h].
-hipError_t launch_router_gemm(const void* x, int x_dtype, const void* wg, int wg_dtype,
-                              float* part, int T, int H, int N, int splits, hipStream_t st);
-int router_splits(int T, int H, int N);
+// Router GEMM plan: the kernel, its K splits and the workspace it needs.
+//   bf16 path (x bf16, H % 32 == 0): the router weight is first written to
+//   the workspace as np bf16 pieces in the tiled fragment layout (np = 3
+//   exact pieces of an fp32 weight, np = 1 for a bf16 weight), then a bf16
+//   MFMA GEMM accumulates x * piece in fp32.
+//   fp32 path (otherwise): fp32 MFMA straight from x and the weight.
+// Logit partials part[s][t][e] = sum over split s of x[t,h] * wg[e,h] go to
+// the workspace when splits > 1 (the route kernel adds them in split order),
+// else straight to the logits.
+struct RouterPlan {
+  int bf16;            // 1: bf16 MFMA over weight pieces, 0: fp32 MFMA
+  int np;              // weight pieces (bf16 path)
+  int npad;            // N rounded up to 16 (rows of each piece)
+  int splits;          // K splits
+  int kchunk;          // K elements per split
+  size_t part_bytes;   // workspace: partials at offset 0 (0 when splits == 1)
+  size_t piece_off;    // workspace: pieces at this offset
+  size_t ws_bytes;     // total workspace
+};
+RouterPlan router_plan(int T, int H, int N, int x_dtype, int wg_dtype);
+// Enqueues the router GEMM; *part_out receives the partials (or the logits
+// when splits == 1) for RouteParams.  ws holds plan.ws_bytes bytes.
+hipError_t launch_router_gemm(const RouterPlan& rp, const void* x, int x_dtype, const void* wg,
+                              int wg_dtype, float* logits, void* ws, int T, int H, int N,
+                              const float** part_out, hipStream_t st);
 
 struct RouteParams {
   const float* part;  // [splits][T][N] logit partials (or the logits, splits = 1)

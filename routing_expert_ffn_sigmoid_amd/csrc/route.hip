@@ -1,4 +1,5 @@
-// route.hip -- router GEMM (fp32 MFMA) and per-token scoring, group-limited
+// route.hip -- router GEMM (bf16 MFMA over exact bf16 pieces of the fp32
+// weight, or fp32 MFMA) and per-token scoring, group-limited
 // top-k and gates (one wavefront per token).
 //
 // Sources: "DeepSeek MoE：从v1到v3的演进" §DeepSeek-v3 (sigmoid score, bias
@@ -7,6 +8,7 @@
 // §1 and §3 (score the groups, keep the best ones, mask the rest, choose the
 // top-k experts); "DeepSeek-V3技术解密…" §四.2 (router kept in fp32).
 #include "moe_internal.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -101,22 +103,275 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const XT* __restrict__
     }
 }
 
-int router_splits(int T, int H, int N) {
-  const int tiles = ((T + 31) / 32) * ((N + 255) / 256);
-  if (tiles <= 0) return 1;
-  int s = (1024 + tiles - 1) / tiles;
-  const int smax = H / 64 < 32 ? H / 64 : 32;
-  if (s > smax) s = smax;
-  if (s < 1) s = 1;
-  return s;
+// ============================================================ router GEMM, bf16 MFMA
+// An fp32 weight w is written as three bf16 pieces with w = hi + mid + lo
+// exactly: hi is w with its low 16 bits cleared, mid the same of r = w - hi,
+// lo = r - mid.  Both differences are exact in fp32 (Sterbenz: the operands
+// share a sign and lie within a factor of two), r keeps at most the 16
+// significand bits below hi's 8, and what mid leaves fits lo's 8 bits, so
+// the pieces hold all 24 bits of w (for |w| >= 2^-103 or w = 0; smaller
+// magnitudes would need subnormal pieces).  A bf16 x bf16 product is exact in
+// fp32, so accumulating x*hi + x*mid + x*lo in fp32 gives the fp32-accumulated
+// dot product of x with the full fp32 weight -- only the order of the fp32
+// additions differs from a plain fp32 GEMM -- at the bf16 MFMA rate.
+//
+// Piece layout (tiled, as the grouped GEMM's weights): piece p is an
+// [npad][H] bf16 matrix at p*npad*H; block (i, j) of 16 rows x 32 columns is
+// the 512 elements at (i*(H/32) + j)*512, chunk l (8 elements) of a block is
+// row 16i + l%16, columns 32j + 8(l/16) .. +7: a wave's MFMA operand for 16
+// experts x 32 k is one contiguous KiB.
+
+__device__ __forceinline__ uint32_t bf16_hi_bits(float v) { return __float_as_uint(v) >> 16; }
+
+// One thread per 8-element chunk: block (i, j) = (id/64) split over
+// npad/16 x H/32 blocks, chunk l = id % 64.
+template <typename WT>
+__global__ __launch_bounds__(256) void router_pieces_kernel(const WT* __restrict__ wg,
+                                                            bf16_t* __restrict__ pieces, int N,
+                                                            int npad, int H) {
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int kb = H / 32;
+  const int64_t nchunks = static_cast<int64_t>(npad) * (H / 8);
+  if (id >= nchunks) return;
+  const int64_t blk = id >> 6;
+  const int l = static_cast<int>(id & 63);
+  const int i = static_cast<int>(blk / kb), j = static_cast<int>(blk % kb);
+  const int r = 16 * i + (l & 15);
+  const int c0 = 32 * j + 8 * (l >> 4);
+  float w[8];
+  if (r < N) {
+    const WT* src = wg + static_cast<int64_t>(r) * H + c0;
+    if constexpr (sizeof(WT) == 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] = __uint_as_float(q[e] << 16);
+        w[2 * e + 1] = __uint_as_float(q[e] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = 0.0f;
+  }
+  const int64_t off = blk * 512 + l * 8;
+  const int64_t pstride = static_cast<int64_t>(npad) * H;
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t h2[2], m2[2], l2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float v = w[2 * e + u];
+      h2[u] = bf16_hi_bits(v);
+      const float rr = v - __uint_as_float(h2[u] << 16);
+      m2[u] = bf16_hi_bits(rr);
+      l2[u] = bf16_hi_bits(rr - __uint_as_float(m2[u] << 16));
+    }
+    hi[e] = h2[0] | (h2[1] << 16);
+    mid[e] = m2[0] | (m2[1] << 16);
+    lo[e] = l2[0] | (l2[1] << 16);
+  }
+  *reinterpret_cast<u32x4*>(pieces + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  if constexpr (sizeof(WT) == 4) {
+    *reinterpret_cast<u32x4*>(pieces + pstride + off) = u32x4{mid[0], mid[1], mid[2], mid[3]};
+    *reinterpret_cast<u32x4*>(pieces + 2 * pstride + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  }
 }
 
-hipError_t launch_router_gemm(const void* x, int x_dtype, const void* wg, int wg_dtype,
-                              float* part, int T, int H, int N, int splits, hipStream_t st) {
+// GEMM: a workgroup of 8 waves owns 256 tokens x 256 experts of one K split;
+// wave (wm, wn) = (wave & 1, wave >> 1) owns token blocks 2j + wm (j < 8) and
+// expert blocks 4wn .. 4wn+3 (16 x 16 each).  k-steps of 32, two LDS stages,
+// both operands loaded global -> LDS directly:
+//   tokens: 256 rows x 64 B per step, 16-byte chunks XOR-swizzled by row
+//           pairs (physical chunk = logical ^ ((row >> 1) & 3));
+//   pieces: np x 16 expert blocks of 1 KiB per step, already in fragment
+//           order.
+// MFMA operands are (weights, tokens), so a lane's accumulator holds four
+// consecutive experts of one token: 16-byte partial stores.
+constexpr int kRtRows = 256;
+constexpr int kRtThreads = 512;
+constexpr int kRtAElems = kRtRows * 32;  // one stage of token rows
+constexpr int kRtBElems = 16 * 512;      // one stage of one piece (256 experts)
+
+template <int NP>
+__global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ pieces, float* __restrict__ part,
+    int T, int H, int N, int npad, int ksteps) {
+  // one array per stage: the compiler then sees that the direct loads into
+  // one stage do not alias the fragment reads of the other, and does not
+  // wait for them before reading
+  __shared__ __attribute__((aligned(16))) bf16_t A0[kRtAElems];
+  __shared__ __attribute__((aligned(16))) bf16_t A1[kRtAElems];
+  __shared__ __attribute__((aligned(16))) bf16_t B0[NP * kRtBElems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1[NP * kRtBElems];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(static_cast<int>(threadIdx.x >> 6));
+  const int wm = wave & 1, wn = wave >> 1;
+  const int t0 = blockIdx.x * kRtRows;
+  const int eb = blockIdx.y * 16;  // first expert block of the tile
+  const int nkb = H / 32;
+  const int k0 = blockIdx.z * ksteps;
+  const int k1 = min(nkb, k0 + ksteps);
+  const int nblk = npad / 16;
+
+  // token rows: wave copies row groups q*8 + wave (16 rows, 1 KiB) per step
+  const int rows = min(kRtRows, T - t0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+      x + static_cast<int64_t>(t0) * H, static_cast<uint32_t>(rows) * static_cast<uint32_t>(H) * 2u);
+  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
+  uint32_t aoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = (q * 8 + wave) * 16 + (lane >> 2);
+    aoff[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(H) * 2u + logical * 16u;
+  }
+  // pieces: wave copies blocks b = q*8 + wave (piece b/16, expert block b%16)
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(pieces, static_cast<uint32_t>(NP) * static_cast<uint32_t>(npad) *
+                            static_cast<uint32_t>(H) * 2u);
+  const uint32_t pbytes = static_cast<uint32_t>(npad) * static_cast<uint32_t>(H) * 2u;
+
+  auto issue = [&](int kb, bf16_t* Ab, bf16_t* Bb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      dma16(rx, aoff[q], static_cast<uint32_t>(kb) * 64u, Ab + (q * 8 + wave) * 512);
+#pragma unroll
+    for (int q = 0; q < 2 * NP; ++q) {
+      const int b = q * 8 + wave;
+      const int blk = eb + (b & 15);
+      if (blk < nblk)  // wave-uniform
+        dma16(rw, lane * 16u,
+              static_cast<uint32_t>(b >> 4) * pbytes +
+                  (static_cast<uint32_t>(blk) * nkb + kb) * 1024u,
+              Bb + b * 512);
+    }
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool active = eb + 4 * wn < nblk;  // wave-uniform: some expert of this wave exists
+
+  // fragment addresses: token row 16*blk + lane%16, logical chunk lane/16
+  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
+  const int aread = (wm * 16 + (lane & 15)) * 32 + ch * 8;
+  const int bread = (4 * wn) * 512 + lane * 8;
+
+  auto compute = [&](const bf16_t* Ab, const bf16_t* Bb) {
+    bf16x8 bf[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        bf[p][nb] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Bb + p * kRtBElems + bread + nb * 512));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 af =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ab + aread + j * 32 * 32));
+#pragma unroll
+      for (int p = NP - 1; p >= 0; --p)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[p][nb], af, acc[j][nb], 0, 0, 0);
+    }
+  };
+  // step kb computes from (Ac, Bc) and loads step kb + 1 into (An, Bn).
+  // Waiting for this wave's loads and crossing the barrier makes every
+  // wave's loads of step kb visible, and tells that no wave still reads the
+  // buffer the next loads overwrite.
+  auto step = [&](int kb, const bf16_t* Ac, const bf16_t* Bc, bf16_t* An, bf16_t* Bn) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + 1 < k1) issue(kb + 1, An, Bn);
+    if (active) compute(Ac, Bc);
+  };
+
+  issue(k0, A0, B0);
+  for (int kb = k0; kb < k1; kb += 2) {
+    step(kb, A0, B0, A1, B1);
+    if (kb + 1 < k1) step(kb + 1, A1, B1, A0, B0);
+  }
+  if (!active) return;
+  // D layout: lane holds experts 4*(lane/16) .. +3 of token lane%16
+  float* out = part + static_cast<int64_t>(blockIdx.z) * T * N;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = t0 + (2 * j + wm) * 16 + (lane & 15);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int e = (eb + 4 * wn + nb) * 16 + 4 * (lane >> 4);
+      if (t < T && e < N) *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * N + e) = acc[j][nb];
+    }
+  }
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+RouterPlan router_plan(int T, int H, int N, int x_dtype, int wg_dtype) {
+  RouterPlan rp{};
+  rp.np = wg_dtype == MOE_F32 ? 3 : 1;
+  rp.npad = (N + 15) / 16 * 16;
+  rp.bf16 = (x_dtype == MOE_BF16 && H % 32 == 0 && T > 0) ? 1 : 0;
+  if (rp.bf16) {
+    const int nkb = H / 32;
+    const int tiles = ((T + kRtRows - 1) / kRtRows) * ((N + 255) / 256);
+    int s = (256 + tiles - 1) / tiles;            // about one workgroup per CU
+    const int smax = nkb / 4 > 1 ? nkb / 4 : 1;   // at least 4 k-steps per split
+    s = s < 1 ? 1 : (s > smax ? smax : s);
+    const int ks = (nkb + s - 1) / s;
+    rp.splits = (nkb + ks - 1) / ks;              // no empty split
+    rp.kchunk = ks * 32;
+  } else {
+    const int tiles = ((T + 31) / 32) * ((N + 255) / 256);
+    int s = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
+    const int smax = H / 64 < 32 ? H / 64 : 32;
+    s = s > smax ? smax : s;
+    rp.splits = s < 1 ? 1 : s;
+    rp.kchunk = ((H + rp.splits - 1) / rp.splits + 15) / 16 * 16;
+  }
+  rp.part_bytes = rp.splits > 1 ? static_cast<size_t>(rp.splits) * T * N * 4 : 0;
+  rp.piece_off = align256(rp.part_bytes);
+  rp.ws_bytes = rp.piece_off + (rp.bf16 ? static_cast<size_t>(rp.np) * rp.npad * H * 2 : 0);
+  return rp;
+}
+
+hipError_t launch_router_gemm(const RouterPlan& rp, const void* x, int x_dtype, const void* wg,
+                              int wg_dtype, float* logits, void* ws, int T, int H, int N,
+                              const float** part_out, hipStream_t st) {
+  float* part = rp.splits > 1 ? static_cast<float*>(ws) : logits;
+  *part_out = part;
   if (T == 0) return hipSuccess;
-  int kchunk = (H + splits - 1) / splits;
-  kchunk = (kchunk + 15) / 16 * 16;
-  dim3 grid((T + 31) / 32, (N + 255) / 256, splits);
+  if (rp.bf16) {
+    bf16_t* pieces = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + rp.piece_off);
+    const int64_t nchunks = static_cast<int64_t>(rp.npad) * (H / 8);
+    const unsigned pgrid = static_cast<unsigned>((nchunks + 255) / 256);
+    if (wg_dtype == MOE_F32)
+      router_pieces_kernel<float><<<pgrid, 256, 0, st>>>(static_cast<const float*>(wg), pieces,
+                                                        N, rp.npad, H);
+    else
+      router_pieces_kernel<bf16_t><<<pgrid, 256, 0, st>>>(static_cast<const bf16_t*>(wg), pieces,
+                                                         N, rp.npad, H);
+    dim3 grid((T + kRtRows - 1) / kRtRows, (N + 255) / 256, rp.splits);
+    const int ks = rp.kchunk / 32;
+    if (rp.np == 3)
+      router_bf16_kernel<3><<<grid, kRtThreads, 0, st>>>(static_cast<const bf16_t*>(x), pieces,
+                                                         part, T, H, N, rp.npad, ks);
+    else
+      router_bf16_kernel<1><<<grid, kRtThreads, 0, st>>>(static_cast<const bf16_t*>(x), pieces,
+                                                         part, T, H, N, rp.npad, ks);
+    return hipGetLastError();
+  }
+  const int kchunk = rp.kchunk;
+  dim3 grid((T + 31) / 32, (N + 255) / 256, rp.splits);
   if (x_dtype == MOE_BF16 && wg_dtype == MOE_F32)
     router_gemm_kernel<bf16_t, float><<<grid, 256, 0, st>>>(
         static_cast<const bf16_t*>(x), static_cast<const float*>(wg), part, T, H, N, kchunk);
