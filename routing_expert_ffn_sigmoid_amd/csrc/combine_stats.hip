@@ -13,6 +13,7 @@ namespace moe {
 // ---------------------------------------------------------------- combine
 // out[t] = y_shared[t] + sum_j gate[t,j] * y_perm[inv_row[t,j]], fp32 sum in
 // slot order, one rounding.  One thread per 8 (bf16) or 4 (fp32) elements.
+constexpr int kCombineSlots = 8;  // row loads in flight per thread
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restrict__ y_perm,
                                                            const int32_t* __restrict__ inv_row,
                                                            const float* __restrict__ gate,
@@ -35,16 +36,37 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
-  for (int j = 0; j < k; ++j) {
-    const int r = inv_row[static_cast<int64_t>(t) * k + j];
-    if (r < 0) continue;
-    const float gj = gate[static_cast<int64_t>(t) * k + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(y_perm + static_cast<int64_t>(r) * H + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // slots in groups of kCombineSlots: row indices and gates first, then all
+  // the group's row loads in flight together, then the sums in slot order
+  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+    int r[kCombineSlots];
+    float g[kCombineSlots];
+    u32x4 v[kCombineSlots];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(gj, __uint_as_float(w[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(gj, __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const int j = j0 + u;
+      r[u] = j < k ? inv_row[static_cast<int64_t>(t) * k + j] : -1;
+      g[u] = j < k ? gate[static_cast<int64_t>(t) * k + j] : 0.f;
+    }
+    // a dropped slot re-reads a kept row of the group (ignored below), so
+    // the loads carry no condition and all go out together; rows are
+    // token-uniform, so these branches do not diverge
+    int any = -1;
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) any = r[u] >= 0 ? r[u] : any;
+    if (any < 0) continue;
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u)
+      v[u] = *reinterpret_cast<const u32x4*>(y_perm + static_cast<int64_t>(r[u] >= 0 ? r[u] : any) * H + c);
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      if (r[u] < 0) continue;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(g[u], __uint_as_float(w[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(g[u], __uint_as_float(w[i] & 0xffff0000u), acc[2 * i + 1]);
+      }
     }
   }
   u32x4 o;
@@ -66,15 +88,34 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   if (c >= H) return;
   f32x4 acc = y_sh ? *reinterpret_cast<const f32x4*>(y_sh + static_cast<int64_t>(t) * H + c)
                    : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int r = inv_row[static_cast<int64_t>(t) * k + j];
-    if (r < 0) continue;
-    const float gj = gate[static_cast<int64_t>(t) * k + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(y_perm + static_cast<int64_t>(r) * H + c);
-    acc.x = fmaf(gj, v.x, acc.x);
-    acc.y = fmaf(gj, v.y, acc.y);
-    acc.z = fmaf(gj, v.z, acc.z);
-    acc.w = fmaf(gj, v.w, acc.w);
+  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+    int r[kCombineSlots];
+    float g[kCombineSlots];
+    f32x4 v[kCombineSlots];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const int j = j0 + u;
+      r[u] = j < k ? inv_row[static_cast<int64_t>(t) * k + j] : -1;
+      g[u] = j < k ? gate[static_cast<int64_t>(t) * k + j] : 0.f;
+    }
+    // a dropped slot re-reads a kept row of the group (ignored below), so
+    // the loads carry no condition and all go out together; rows are
+    // token-uniform, so these branches do not diverge
+    int any = -1;
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) any = r[u] >= 0 ? r[u] : any;
+    if (any < 0) continue;
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(y_perm + static_cast<int64_t>(r[u] >= 0 ? r[u] : any) * H + c);
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      if (r[u] < 0) continue;
+      acc.x = fmaf(g[u], v[u].x, acc.x);
+      acc.y = fmaf(g[u], v[u].y, acc.y);
+      acc.z = fmaf(g[u], v[u].z, acc.z);
+      acc.w = fmaf(g[u], v[u].w, acc.w);
+    }
   }
   *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * H + c) = acc;
 }
@@ -121,13 +162,21 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   const int t0 = b * chunk;
   const int t1 = min(T, t0 + chunk);
   double* out = part + static_cast<int64_t>(b) * (N + 2);
+  auto score = [&](float l, int t) {
+    return score_fn == MOE_SCORE_SIGMOID ? sigmoid_score(l) : __expf(l - lse[t]);
+  };
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    // tokens in ascending order; eight logit loads in flight at a time
     double acc = 0.0;
-    for (int t = t0; t < t1; ++t) {
-      const float l = logits[static_cast<int64_t>(t) * N + e];
-      const float s = score_fn == MOE_SCORE_SIGMOID ? sigmoid_score(l) : __expf(l - lse[t]);
-      acc += static_cast<double>(s);
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {
+      float l[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) l[u] = logits[static_cast<int64_t>(t + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += static_cast<double>(score(l[u], t + u));
     }
+    for (; t < t1; ++t) acc += static_cast<double>(score(logits[static_cast<int64_t>(t) * N + e], t));
     out[e] = acc;
   }
   if (threadIdx.x < 64) {
@@ -166,9 +215,32 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const double* __restri
                                                           float* __restrict__ scalars) {
   __shared__ double sh[4];
   const int e = threadIdx.x;
+  // column sums in block order, eight partial loads in flight at a time
   double col = 0.0;
-  if (e < N)
-    for (int b = 0; b < nblk; ++b) col += part[static_cast<int64_t>(b) * (N + 2) + e];
+  if (e < N) {
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[static_cast<int64_t>(b + u) * (N + 2) + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) col += v[u];
+    }
+    for (; b < nblk; ++b) col += part[static_cast<int64_t>(b) * (N + 2) + e];
+  }
+  // lse sums: lane l of wave 0 takes blocks l, l + 64, ...
+  double z = 0.0, z2 = 0.0;
+  if (threadIdx.x < 64) {
+    for (int b = threadIdx.x; b < nblk; b += 64) {
+      z += part[static_cast<int64_t>(b) * (N + 2) + N];
+      z2 += part[static_cast<int64_t>(b) * (N + 2) + N + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      z += __shfl_xor(z, o, kWave);
+      z2 += __shfl_xor(z2, o, kWave);
+    }
+  }
   const double tot = block_sum_f64(col, sh);
   const double fe = (e < N && T > 0 && k > 0) ? static_cast<double>(counts[e]) / (static_cast<double>(k) * T) : 0.0;
   const double pe = (e < N && tot > 0.0) ? col / tot : 0.0;
@@ -178,11 +250,6 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const double* __restri
     if (P) P[e] = static_cast<float>(pe);
   }
   if (e == 0 && scalars) {
-    double z = 0.0, z2 = 0.0;
-    for (int b = 0; b < nblk; ++b) {
-      z += part[static_cast<int64_t>(b) * (N + 2) + N];
-      z2 += part[static_cast<int64_t>(b) * (N + 2) + N + 1];
-    }
     scalars[0] = static_cast<float>(N * lb);
     scalars[1] = T > 0 ? static_cast<float>(z / T) : 0.f;
     scalars[2] = T > 0 ? static_cast<float>(z2 / T) : 0.f;
