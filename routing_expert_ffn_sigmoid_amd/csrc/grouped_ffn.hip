@@ -203,12 +203,16 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__
   u32x4 bbuf[NSLOT][2][4];
   u32x4 areg[APASS];
 
+  // each weight byte is read once, by this wave only: the loads carry the
+  // non-temporal hint (measured on the V3 decode layer: gate/up 2.30 ->
+  // 2.10 ms, 6.6 TB/s; down 1.14 -> 1.09 ms)
   auto load_b = [&](int step, u32x4 (&dst)[2][4]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        dst[ks][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + (step * 2 + ks) * kTileElems);
+        dst[ks][nb] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(bptr[nb] + (step * 2 + ks) * kTileElems));
   };
   auto load_a = [&](int step) {
 #pragma unroll
