@@ -771,12 +771,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 }
 
 // ---------------------------------------------------------------------
-// 4-stage variant (k-steps of 32): three stages of both operands are in
-// flight per CU while the fourth is consumed.  Each wave waits for its own
-// loads of the stage it is about to read (s_waitcnt vmcnt) *before* the
-// workgroup barrier, so after the barrier every wave's share of that stage
-// is in LDS; the barrier also retires the reads of the buffer the next load
-// overwrites.  Used when K is a multiple of 128.
+// 4-stage variant (k-steps of 32), four LDS buffers of both operands.  The
+// workgroup barrier closes each step: before it every wave waits for its
+// own loads of the stage after next (s_waitcnt vmcnt), so after it that
+// stage is in LDS for all waves, and the buffer the finished step read is
+// free for the stage four steps ahead (two steps of load latency are then
+// covered).  Because the next stage is already visible during a step, the
+// step's last M-blocks also read the next step's first fragments (four
+// weight, two activation), and the MFMAs after the barrier start without
+// waiting on LDS.  A tile ends with that barrier, so the next tile may load
+// all four buffers at once.  Used when K is a multiple of 128.
 // ---------------------------------------------------------------------
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
@@ -795,36 +799,81 @@ constexpr int kBig4MaxNmbw = kBig4Rows / 32;
 constexpr int kBuf4AElems = kBig4Rows * kBK4;
 
 
+// first fragments of a step: the four weight fragments and the first two
+// activation fragments
 template <int NMBW, bool SWIGLU>
-__device__ __forceinline__ void big4_compute(const bf16_t* __restrict__ Ab,
-                                             const bf16_t* __restrict__ Bb,
-                                             f32x4 (&acc)[NMBW][4], int wm, int wn) {
+__device__ __forceinline__ void big4_first(const bf16_t* __restrict__ Ab,
+                                           const bf16_t* __restrict__ Bb, int wm, int wn,
+                                           bf16x8 (&bf)[4], bf16x8 (&a01)[2]) {
   const int lane = threadIdx.x & 63;
-  // fragment row = 16*block + lane%16; swizzle term ((row >> 1) & 3) is
-  // ((lane%16) >> 1) & 3: one base per operand, block offsets are immediates
   const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
   const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
-  const bf16_t* bbase = Bb + lane * 8;  // weight slots are in fragment order
-  bf16x8 bf[4];
+  const bf16_t* bbase = Bb + lane * 8;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
     bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * kTileElems));
+  a01[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase));
+  a01[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (NMBW > 1 ? 32 * kBK4 : 0)));
+}
+
+// One k-step from (bf, a01) and the rest of buffer Ab; during the last two
+// M-blocks the next step's first fragments are read from (An, Bn) into
+// (bf, a01), so the MFMAs after the next barrier start at once.
+template <int NMBW, bool SWIGLU>
+__device__ __forceinline__ void big4_step(const bf16_t* __restrict__ Ab,
+                                          const bf16_t* __restrict__ An,
+                                          const bf16_t* __restrict__ Bn,
+                                          f32x4 (&acc)[NMBW][4], int wm, int wn,
+                                          bf16x8 (&bf)[4], bf16x8 (&a01)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
+  const int aoffs = (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
+  const bf16_t* abase = Ab + aoffs;
+  const bf16_t* anext = An + aoffs;
+  const bf16_t* bnext = Bn + lane * 8;
   bf16x8 af[NMBW];
-#pragma unroll
-  for (int j = 0; j < kReadAhead && j < NMBW; ++j)
-    af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * kBK4));
+  af[0] = a01[0];
+  if (NMBW > 1) af[1] = a01[1];
+  bf16x8 nbf[4], na[2];
+  constexpr int J0 = NMBW >= 2 ? NMBW - 2 : 0;
 #pragma unroll
   for (int j = 0; j < NMBW; ++j) {
-    if (j + kReadAhead < NMBW)
-      af[j + kReadAhead] =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (j + kReadAhead) * 32 * kBK4));
+    if (j + 2 < NMBW)
+      af[j + 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (j + 2) * 32 * kBK4));
+    if (j == J0) {
+      nbf[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 0) * kTileElems));
+      nbf[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 1) * kTileElems));
+      nbf[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 2) * kTileElems));
+    }
+    if (j == NMBW - 1) {
+      nbf[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 3) * kTileElems));
+      na[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(anext));
+      na[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(anext + (NMBW > 1 ? 32 * kBK4 : 0)));
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
   }
-  fragment_issue_order<NMBW>();
+  // issue order: per M-block 2 MFMAs, the block's LDS reads, 2 MFMAs
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j) {
+    const int nreads = (j + 2 < NMBW ? 1 : 0) + (j == J0 ? 3 : 0) + (j == NMBW - 1 ? 3 : 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    switch (nreads) {
+      case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
+      case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
+      case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
+      case 6: __builtin_amdgcn_sched_group_barrier(0x100, 6, 0); break;
+      case 7: __builtin_amdgcn_sched_group_barrier(0x100, 7, 0); break;
+      default: break;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) bf[nb] = nbf[nb];
+  a01[0] = na[0];
+  a01[1] = na[1];
 }
-
 template <int NMBW, bool SWIGLU>
 __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
                                        bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
@@ -893,37 +942,42 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the barrier closes each step: after it, the next stage (waited for
+  // before it) is visible and the buffer the step read is free for the
+  // stage four steps ahead
   issue(0, A0, B0);
   mark[0] = cnt;
   issue(1, A1, B1);
   mark[1] = cnt;
   issue(2, A2, B2);
   mark[2] = cnt;
+  issue(3, A3, B3);
+  mark[3] = cnt;
+  wait_stage(1);
+  __builtin_amdgcn_s_barrier();
+  bf16x8 bf[4], a01[2];
+  big4_first<NMBW, SWIGLU>(A0, B0, wm, wn, bf, a01);
   for (int st = 0; st < nk; st += kStages) {
-    // step st (buffer 0)
-    wait_stage(0);
-    __builtin_amdgcn_s_barrier();
-    if (st + 3 < nk) issue(st + 3, A3, B3);
-    mark[3] = cnt;
-    big4_compute<NMBW, SWIGLU>(A0, B0, acc, wm, wn);
-    // step st+1 (buffer 1)
-    wait_stage(1);
+    big4_step<NMBW, SWIGLU>(A0, A1, B1, acc, wm, wn, bf, a01);
+    wait_stage(2);
     __builtin_amdgcn_s_barrier();
     if (st + 4 < nk) issue(st + 4, A0, B0);
     mark[0] = cnt;
-    big4_compute<NMBW, SWIGLU>(A1, B1, acc, wm, wn);
-    // step st+2 (buffer 2)
-    wait_stage(2);
+    big4_step<NMBW, SWIGLU>(A1, A2, B2, acc, wm, wn, bf, a01);
+    wait_stage(3);
     __builtin_amdgcn_s_barrier();
     if (st + 5 < nk) issue(st + 5, A1, B1);
     mark[1] = cnt;
-    big4_compute<NMBW, SWIGLU>(A2, B2, acc, wm, wn);
-    // step st+3 (buffer 3)
-    wait_stage(3);
+    big4_step<NMBW, SWIGLU>(A2, A3, B3, acc, wm, wn, bf, a01);
+    wait_stage(0);
     __builtin_amdgcn_s_barrier();
     if (st + 6 < nk) issue(st + 6, A2, B2);
     mark[2] = cnt;
-    big4_compute<NMBW, SWIGLU>(A3, B3, acc, wm, wn);
+    big4_step<NMBW, SWIGLU>(A3, A0, B0, acc, wm, wn, bf, a01);
+    wait_stage(1);
+    __builtin_amdgcn_s_barrier();
+    if (st + 7 < nk) issue(st + 7, A3, B3);
+    mark[3] = cnt;
   }
   big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
 }
@@ -1047,11 +1101,16 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   if (grid > ub8) grid = ub8;
   grid = (grid + 7) / 8 * 8;
   bool k128 = true;  // the 4-stage kernel consumes 4 k-steps of 32 per iteration
-  for (int i = 0; i < fl.ngroups; ++i) k128 = k128 && fl.g[i].K % 128 == 0;
-  // measured on the V3-shaped prefill layer: the 4-stage pipeline wins on the
-  // long-K gate/up phase (K = hidden), the 2-stage one on the down phase
-  // (K = expert width, fewer k-steps per tile to amortise the deeper fill)
-  k128 = k128 && phase == 0;
+  bool klong = true;
+  for (int i = 0; i < fl.ngroups; ++i) {
+    k128 = k128 && fl.g[i].K % 128 == 0;
+    klong = klong && fl.g[i].K >= 2048;
+  }
+  // measured: the 4-stage pipeline wins on the gate/up phase (K = hidden)
+  // and on a down phase with K >= 2048 (V3: 2.84 -> 2.73 ms); with shorter K
+  // (v1, K = 1408: 44 k-steps per tile) the persistent 2-stage kernel, which
+  // overlaps a tile's first loads with the previous tile, is faster
+  k128 = k128 && (phase == 0 || klong);
 #ifndef MOE_FFN_NO_BIG4
   if (k128) {
     if (phase == 0)

@@ -173,12 +173,15 @@ def test_bf16_small_layer_parity_and_determinism():
         assert torch.equal(aux[n], aux2[n]), n
 
 
-@pytest.mark.parametrize("rows_per_seg", [5, 40, 150, 400])
-def test_grouped_ffn_ragged_segments(rows_per_seg):
-    """moe_grouped_ffn alone: ragged and empty segments, every tile height."""
+@pytest.mark.parametrize("rows_per_seg,inter", [(5, 192), (40, 192), (150, 192), (400, 192),
+                                                 (150, 2048), (400, 2048)])
+def test_grouped_ffn_ragged_segments(rows_per_seg, inter):
+    """moe_grouped_ffn alone: ragged and empty segments, every tile height;
+    an expert width of 2048 sends the down projection of large segments
+    through the 4-stage kernel (K >= 2048), 192 through the 2-stage one."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
-    nseg, H, inter = 9, 256, 192
+    nseg, H = 9, 256
     sizes = rng.integers(0, 2 * rows_per_seg, size=nseg)
     sizes[2] = 0
     sizes[5] = 3 * rows_per_seg + 7
@@ -186,7 +189,7 @@ def test_grouped_ffn_ragged_segments(rows_per_seg):
     M = int(offs[-1])
     wl = workloads.V3_PREFILL.with_(H=H, N=16, n_groups=1, topk_groups=1, k=2, I=64)
     cfg = moe.make_cfg(wl)
-    say(f"grouped ffn: sizes={sizes.tolist()}")
+    say(f"grouped ffn: inter={inter} sizes={sizes.tolist()}")
     a = synth.normal((M, H), 1.0, torch.bfloat16, "cuda", 1, "a")
     w13 = synth.normal((nseg, 2 * inter, H), 0.02, torch.bfloat16, "cuda", 1, "w13")
     w2 = synth.normal((nseg, H, inter), 0.02, torch.bfloat16, "cuda", 1, "w2")
