@@ -786,17 +786,13 @@ constexpr int kBK4 = 32;
 constexpr int kStages = 4;
 constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
 // Activation rows per tile of the 4-stage kernel (a multiple of 32, at most
-// 384).  Taller tiles keep an expert slightly over 256 rows in one tile, but
-// on the V3-shaped prefill layer 320 measured 2 % slower than 256 (fewer,
-// less even tiles per CU; the two halves of a split expert already share its
-// weights through L2).
-#ifndef MOE_FFN_BIG4_ROWS
-#define MOE_FFN_BIG4_ROWS 256
-#endif
-constexpr int kBig4Rows = MOE_FFN_BIG4_ROWS;
-static_assert(kBig4Rows % 32 == 0 && kBig4Rows <= 384, "tile rows");
-constexpr int kBig4MaxNmbw = kBig4Rows / 32;
-constexpr int kBuf4AElems = kBig4Rows * kBK4;
+// 384), per phase.  Taller tiles keep an expert slightly over 256 rows in
+// one tile and load its weights once; measured on the V3-shaped layers, 320
+// rows are 2-4 % faster than 256 on the down phase (K = 2048) but 6 % slower
+// on gate/up (K = 7168, where the taller tile's longer register-bound steps
+// cost more than the saved weight loads).
+constexpr int kBig4RowsGateUp = 256;
+constexpr int kBig4RowsDown = 320;
 
 
 // first fragments of a step: the four weight fragments and the first two
@@ -982,12 +978,30 @@ __device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mro
   big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
 }
 
-template <bool SWIGLU>
+// big4_tile for the instantiated height covering nmbw M-blocks per wave
+template <int N, bool SWIGLU>
+__device__ __forceinline__ void big4_dispatch(int nmbw, const FfnGroup& g, int s, int nt,
+                                              int mrow0, int mv, bf16_t* A0, bf16_t* A1,
+                                              bf16_t* A2, bf16_t* A3, bf16_t* B0, bf16_t* B1,
+                                              bf16_t* B2, bf16_t* B3) {
+  if constexpr (N > 1) {
+    if (nmbw >= N) {
+      big4_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+      return;
+    }
+    big4_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  } else {
+    big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  }
+}
+
+template <bool SWIGLU, int ROWS>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
-  __shared__ __attribute__((aligned(16))) bf16_t A0[kBuf4AElems];
-  __shared__ __attribute__((aligned(16))) bf16_t A1[kBuf4AElems];
-  __shared__ __attribute__((aligned(16))) bf16_t A2[kBuf4AElems];
-  __shared__ __attribute__((aligned(16))) bf16_t A3[kBuf4AElems];
+  static_assert(ROWS % 32 == 0 && ROWS <= 384, "tile rows");
+  __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
   __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
@@ -996,7 +1010,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
   __shared__ int tmp[kThreads];
 
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
-  if (threadIdx.x < kThreads) build_tile_starts<kBig4Rows>(a, nsegT, tstart, tmp);
+  if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
   else build_tile_starts_idle();
   const int total = tstart[nsegT];
   const int nxcd = 8;
@@ -1018,7 +1032,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int s = grp ? i0 - a.g[0].nseg : i0;
     const int r0 = seg_begin(g, s);
     const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + kBig4Rows - 1) / kBig4Rows;
+    const int mtc = (rows + ROWS - 1) / ROWS;
     const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
     const int local = L - tstart[i0];
     int nt, mt;
@@ -1026,28 +1040,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
     const int mrow0 = r0 + mt * rpt;
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
-    switch (nmbw) {
-#if MOE_FFN_BIG4_ROWS > 352
-      case 12: big4_tile<12, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-#endif
-#if MOE_FFN_BIG4_ROWS > 320
-      case 11: big4_tile<11, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-#endif
-#if MOE_FFN_BIG4_ROWS > 288
-      case 10: big4_tile<10, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-#endif
-#if MOE_FFN_BIG4_ROWS > 256
-      case 9: big4_tile<9, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-#endif
-      case 8: big4_tile<8, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 7: big4_tile<7, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 6: big4_tile<6, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 5: big4_tile<5, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 4: big4_tile<4, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 3: big4_tile<3, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      case 2: big4_tile<2, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-      default: big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3); break;
-    }
+    big4_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
     __syncthreads();
   }
 }
@@ -1114,9 +1107,9 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
 #ifndef MOE_FFN_NO_BIG4
   if (k128) {
     if (phase == 0)
-      ffn_big4_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+      ffn_big4_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     else
-      ffn_big4_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+      ffn_big4_kernel<false, kBig4RowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
 #endif
