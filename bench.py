@@ -241,7 +241,8 @@ def summarize_profile(d: str, workload: str, commands: dict):
     txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
     with open(txt, "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    gate_up = [k for k in traffic if "true>" in k and "ffn" in k]
+    # gate/up launches: the SwiGLU instantiation (template argument `true`)
+    gate_up = [k for k in traffic if "ffn" in k and "true" in k[k.find("<"):]]
     if gate_up:
         k = max(gate_up, key=lambda n: avg.get(n, 0.0))
         src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")
