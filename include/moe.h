@@ -182,7 +182,11 @@ moe_status moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  *            and the router GEMM is skipped
  *   w_router [N,H] router_dtype (ignored when x == NULL)
  *   logits   [T,N] f32: written when x != NULL (fp32-accumulated x.W_g^T,
- *            [TECH] §四.2 keeps the router in fp32)
+ *            [TECH] §四.2 keeps the router in fp32).  With bf16 x the
+ *            weight is first written to the workspace as bf16 pieces that
+ *            sum to it exactly (three for an fp32 weight); each bf16 x bf16
+ *            product is exact in fp32, so only the order of the fp32
+ *            additions differs from an fp32 GEMM.
  *   bias     [N] f32 or NULL: added to the score for selection only
  *   topk_idx [T,k] i32: chosen experts, slot j = j-th largest key; ties go
  *            to the lower expert (and group) index
@@ -197,7 +201,10 @@ moe_status moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  * device-limited routing ([EVO] §DeepSeek-v2): with one group per device,
  * the kept groups are exactly the devices met first when walking the
  * experts from the highest key down, so a token reaches at most
- * topk_groups devices.  Workspace: moe_workspace_size. */
+ * topk_groups devices.  Workspace: moe_workspace_size bytes suffice; with
+ * x != NULL the router GEMM's partial sums and weight pieces live there
+ * (MOE_ERR_WORKSPACE if ws is NULL or smaller), with x == NULL none is
+ * used. */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
                      float* logits, const float* bias, int32_t* topk_idx,
                      float* topk_gate, float* topk_score, float* token_lse,

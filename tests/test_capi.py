@@ -111,6 +111,14 @@ def test_missing_workspace_and_pointers_rejected():
                          None, None, 0, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_grouped_ffn(ctypes.byref(cfg), 0, None, 4, 64, fake, None, fake, fake, fake,
                              fake, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    # the router GEMM needs workspace: K-split partials, and with bf16
+    # activations the bf16 pieces of the router weight even when K is not
+    # split (6 k-steps of 32 below); checked before any launch
+    for c in (cfg, moe.make_cfg(workloads.V1, T=300, H=192)):
+        assert L.moe_route(ctypes.byref(c), fake, fake, fake, None, fake, fake, fake, None,
+                           fake, 16, None) == moe.MOE_ERR_WORKSPACE
+        rc, need = _ws_size(c)
+        assert rc == moe.MOE_OK and need > 16
     n = ctypes.c_size_t(0)
     assert L.moe_workspace_size(ctypes.byref(cfg), None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_size(None, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
