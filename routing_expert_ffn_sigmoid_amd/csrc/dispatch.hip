@@ -20,7 +20,7 @@
 
 namespace moe {
 
-constexpr int kTokPerBlock = 256;  // 4 waves x 64 tokens
+constexpr int kTokPerBlock = kDispatchTokPerBlock;  // 4 waves x 64 tokens
 
 int dispatch_blocks(int T) { return (T + kTokPerBlock - 1) / kTokPerBlock; }
 
@@ -378,17 +378,26 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
   if (i < n) p[i] = v;
 }
 
+hipError_t launch_zero_block_counts(const DispatchWs& w, int T, int N, hipStream_t st) {
+  const int nb = dispatch_blocks(T);
+  if (nb > 0) fill_i32_kernel<<<(nb * N + 255) / 256, 256, 0, st>>>(w.block_counts, nb * N, 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
                            int k, const DropPolicy& d, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
-                           const DispatchWs& w, hipStream_t st) {
+                           const DispatchWs& w, hipStream_t st, bool counts_ready) {
   const int nb = dispatch_blocks(T);
   const size_t lds = 4 * N * sizeof(unsigned long long);
   const bool grouped = d.group_cap > 0;
-  if (nb > 0 && k > 0)
+  if (counts_ready) {
+    // per-block counts were added up by the route kernel
+  } else if (nb > 0 && k > 0) {
     dispatch_count_kernel<<<nb, 256, lds, st>>>(topk_idx, T, N, k, w.block_counts);
-  else if (nb > 0)
+  } else if (nb > 0) {
     fill_i32_kernel<<<(nb * N + 255) / 256, 256, 0, st>>>(w.block_counts, nb * N, 0);
+  }
   // with group dropping the offsets and drop counts written here are
   // provisional (no drops); kept_scan_kernel overwrites them
   dispatch_scan_kernel<<<1, 256, 0, st>>>(w.block_counts, nb, N, grouped ? 0 : d.capacity,

@@ -429,20 +429,23 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
   const float* part = logits;
   MOE_TRY(launch_router_gemm(L.rp, x, cfg->act_dtype, w->w_router, cfg->router_dtype, logits,
                              at<char>(ws, L.router), T, cfg->H, N, &part, st));
-  // 2. scores, group limit, top-k, gates
+  // 2. scores, group limit, top-k, gates; the route kernel also adds up the
+  // per-block expert counts of dispatch (route -> dispatch fusion)
   record(aux, MOE_STAGE_ROUTE, st);
+  const DropPolicy dp = drop_policy(cfg);
+  DispatchWs dw = dispatch_ws_carve(at<char>(ws, L.disp), T, N, k, dp);
+  MOE_TRY(launch_zero_block_counts(dw, T, N, st));
   RouteParams p{};
   p.part = part; p.splits = L.rp.splits; p.logits = logits; p.bias = bias; p.topk_idx = idx;
   p.topk_gate = gate; p.topk_score = score; p.token_lse = lse; p.T = T; p.N = N; p.k = k;
   p.n_groups = cfg->n_groups; p.topk_groups = cfg->topk_groups; p.group_topn = cfg->group_topn;
   p.score_fn = cfg->score_fn; p.norm_topk = cfg->norm_topk; p.route_scale = cfg->route_scale;
+  p.block_counts = dw.block_counts;
   MOE_TRY(launch_route(p, st));
   // 3. dispatch (the row gather itself is fused into the gate/up loads)
   record(aux, MOE_STAGE_DISPATCH, st);
-  const DropPolicy dp = drop_policy(cfg);
-  DispatchWs dw = dispatch_ws_carve(at<char>(ws, L.disp), T, N, k, dp);
   MOE_TRY(launch_dispatch(idx, score, T, N, k, dp, counts, offsets, row_token, inv_row, ndrop, dw,
-                          st));
+                          st, /*counts_ready=*/true));
   // 4. experts
   void* y_r = at<char>(ws, L.y_r);
   void* y_s = cfg->n_shared > 0 ? at<char>(ws, L.y_s) : nullptr;

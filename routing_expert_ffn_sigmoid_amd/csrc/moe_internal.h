@@ -131,6 +131,10 @@ hipError_t launch_router_gemm(const RouterPlan& rp, const void* x, int x_dtype, 
                               int wg_dtype, float* logits, void* ws, int T, int H, int N,
                               const float** part_out, hipStream_t st);
 
+// Tokens per dispatch block: the dispatch kernels count and rank each
+// expert's assignments per block of this many tokens.
+constexpr int kDispatchTokPerBlock = 256;
+
 struct RouteParams {
   const float* part;  // [splits][T][N] logit partials (or the logits, splits = 1)
   int splits;
@@ -140,6 +144,11 @@ struct RouteParams {
   float* topk_gate;
   float* topk_score;
   float* token_lse;   // may be null
+  // when not null: [ceil(T / kDispatchTokPerBlock)][N] per-block expert
+  // counts, zero on entry; the route kernel adds its selections (integer
+  // adds, so the counts do not depend on their order) and dispatch then
+  // skips its counting pass
+  int32_t* block_counts;
   int T, N, k, n_groups, topk_groups, group_topn, score_fn, norm_topk;
   float route_scale;
 };
@@ -166,10 +175,14 @@ struct DispatchWs {
 int dispatch_blocks(int T);
 size_t dispatch_ws_bytes(int T, int N, int k, const DropPolicy& d);
 DispatchWs dispatch_ws_carve(void* ws, int T, int N, int k, const DropPolicy& d);
+// zero the per-block counts the fused route kernel accumulates into
+hipError_t launch_zero_block_counts(const DispatchWs& w, int T, int N, hipStream_t st);
+// counts_ready: w.block_counts already holds the per-block counts of
+// topk_idx (route kernel with RouteParams::block_counts)
 hipError_t launch_dispatch(const int32_t* topk_idx, const float* topk_score, int T, int N,
                            int k, const DropPolicy& d, int32_t* counts, int32_t* offsets,
                            int32_t* row_token, int32_t* inv_row, int32_t* n_dropped,
-                           const DispatchWs& w, hipStream_t st);
+                           const DispatchWs& w, hipStream_t st, bool counts_ready = false);
 hipError_t launch_permute(const void* x, int elem_bytes, int H, const int32_t* row_token,
                           const int32_t* offsets, int N, int max_rows, void* x_perm,
                           hipStream_t st);

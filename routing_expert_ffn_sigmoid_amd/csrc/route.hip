@@ -521,6 +521,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
     p.topk_idx[o] = my_idx;
     p.topk_gate[o] = g * p.route_scale;
     p.topk_score[o] = my_s;
+    // fused dispatch count: one integer add per selection into the token's
+    // dispatch block (the sum does not depend on the order of the adds)
+    if (p.block_counts)
+      atomicAdd(&p.block_counts[static_cast<int64_t>(t / kDispatchTokPerBlock) * p.N + my_idx], 1);
   }
   if (lane == 0 && p.token_lse) p.token_lse[t] = lse;
 }

@@ -256,10 +256,15 @@ def test_combine_and_bias_update_match_oracle():
     np.testing.assert_array_equal(bt.cpu().numpy(), oracle.bias_update(counts, bias, 0.001))
 
 
-def test_granular_calls_compose_to_layer_forward():
-    """route -> permute -> grouped_ffn -> combine gives the layer's output."""
+@pytest.mark.parametrize("T", [96, 600])
+def test_granular_calls_compose_to_layer_forward(T):
+    """route -> permute -> grouped_ffn -> combine gives the layer's output, and
+    the layer's fused route -> dispatch counting (per-block expert counts
+    added up by the route kernel) gives exactly the dispatch of the granular
+    calls, whose moe_permute counts on its own; T = 600 spans three dispatch
+    blocks of 256 tokens."""
     require_gpu()
-    wl = workloads.TINY.with_(T=96, n_shared=0)
+    wl = workloads.TINY.with_(T=T, n_shared=0)
     cfg = moe.make_cfg(wl)
     inp = make_inputs(wl)
     out_ref, aux = layer_forward(wl, inp)
@@ -280,6 +285,9 @@ def test_granular_calls_compose_to_layer_forward():
     torch.cuda.synchronize()
     M = int(offs[-1])
     assert torch.equal(xp[:M], inp["x"][rt[:M].long()])
+    for name, got in (("counts", counts), ("offsets", offs), ("inv_row", inv)):
+        assert torch.equal(got, aux[name]), name
+    assert torch.equal(rt[:M], aux["row_token"][:M])
     y = torch.empty((T * k, H), device=dev)
     ws2 = torch.empty(moe.moe_grouped_ffn_workspace_size(cfg, T * k, wl.I), dtype=torch.uint8,
                       device=dev)
