@@ -142,7 +142,8 @@ enum {
  *   every assignment dropped}, f [N], P [N], scalars [3] f32 = {L_B, z, z_sq}.
  * stage_events: host array of MOE_N_STAGES+1 hipEvent_t created by the
  * caller; event i is recorded on the stream before stage i and event
- * MOE_N_STAGES after the last stage.  NULL = no events. */
+ * MOE_N_STAGES after the last stage.  NULL = no events.  A failed event
+ * record returns MOE_ERR_HIP like a failed launch. */
 typedef struct {
   float* logits;
   int32_t* topk_idx;

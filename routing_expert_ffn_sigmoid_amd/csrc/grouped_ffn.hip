@@ -376,7 +376,6 @@ __global__ __launch_bounds__(kThreads, MOE_FFN_MINBLK) void ffn_bf16_kernel(FfnL
 // weights cost the same and stream them through L2 together.
 // =====================================================================
 constexpr int kBigRows = 256;   // max rows per tile
-constexpr int kBigCols = 256;   // weight rows per tile
 constexpr int kBigBufElems = 256 * kBK;
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
@@ -1050,8 +1049,7 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st);
 static int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
-  hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (!cus[dev]) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)

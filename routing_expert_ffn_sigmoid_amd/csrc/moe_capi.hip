@@ -125,9 +125,10 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
     if (e_ != hipSuccess) return MOE_ERR_HIP;           \
   } while (0)
 
-void record(const moe_aux* aux, int i, hipStream_t st) {
+hipError_t record(const moe_aux* aux, int i, hipStream_t st) {
   if (aux && aux->stage_events && aux->stage_events[i])
-    hipEventRecord(static_cast<hipEvent_t>(aux->stage_events[i]), st);
+    return hipEventRecord(static_cast<hipEvent_t>(aux->stage_events[i]), st);
+  return hipSuccess;
 }
 
 // Gate/up (phase 0) and down (phase 1) over the routed segments and the
@@ -176,15 +177,15 @@ moe_status run_ffn(const moe_cfg* c, const void* x, const int32_t* row_token,
     g1[n] = b;
     ++n;
   }
-  record(aux, MOE_STAGE_FFN_GATE_UP, st);
+  MOE_TRY(record(aux, MOE_STAGE_FFN_GATE_UP, st));
   if (c->act_dtype == MOE_BF16) {
     const int hint = routed ? TK / c->N : c->T;
     if (n) MOE_TRY(launch_ffn_bf16(g0, n, 0, hint, st));
-    record(aux, MOE_STAGE_FFN_DOWN, st);
+    MOE_TRY(record(aux, MOE_STAGE_FFN_DOWN, st));
     if (n) MOE_TRY(launch_ffn_bf16(g1, n, 1, hint, st));
   } else {
     for (int i = 0; i < n; ++i) MOE_TRY(launch_ffn_f32(g0[i], 0, g0[i].rows, st));
-    record(aux, MOE_STAGE_FFN_DOWN, st);
+    MOE_TRY(record(aux, MOE_STAGE_FFN_DOWN, st));
     for (int i = 0; i < n; ++i) MOE_TRY(launch_ffn_f32(g1[i], 1, g1[i].rows, st));
   }
   return MOE_OK;
@@ -425,13 +426,13 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
   float* scalars = pick(aux ? aux->scalars : static_cast<float*>(nullptr), L.scalars);
 
   // 1. router GEMM
-  record(aux, MOE_STAGE_ROUTER_GEMM, st);
+  MOE_TRY(record(aux, MOE_STAGE_ROUTER_GEMM, st));
   const float* part = logits;
   MOE_TRY(launch_router_gemm(L.rp, x, cfg->act_dtype, w->w_router, cfg->router_dtype, logits,
                              at<char>(ws, L.router), T, cfg->H, N, &part, st));
   // 2. scores, group limit, top-k, gates; the route kernel also adds up the
   // per-block expert counts of dispatch (route -> dispatch fusion)
-  record(aux, MOE_STAGE_ROUTE, st);
+  MOE_TRY(record(aux, MOE_STAGE_ROUTE, st));
   const DropPolicy dp = drop_policy(cfg);
   DispatchWs dw = dispatch_ws_carve(at<char>(ws, L.disp), T, N, k, dp);
   MOE_TRY(launch_zero_block_counts(dw, T, N, st));
@@ -443,7 +444,7 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
   p.block_counts = dw.block_counts;
   MOE_TRY(launch_route(p, st));
   // 3. dispatch (the row gather itself is fused into the gate/up loads)
-  record(aux, MOE_STAGE_DISPATCH, st);
+  MOE_TRY(record(aux, MOE_STAGE_DISPATCH, st));
   MOE_TRY(launch_dispatch(idx, score, T, N, k, dp, counts, offsets, row_token, inv_row, ndrop, dw,
                           st, /*counts_ready=*/true));
   // 4. experts
@@ -453,13 +454,13 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
               st, aux);
   if (s != MOE_OK) return s;
   // 5. combine
-  record(aux, MOE_STAGE_COMBINE, st);
+  MOE_TRY(record(aux, MOE_STAGE_COMBINE, st));
   MOE_TRY(launch_combine(y_r, inv_row, gate, y_s, out, T, cfg->H, k, cfg->act_dtype, st));
   // 6. load statistics
-  record(aux, MOE_STAGE_STATS, st);
+  MOE_TRY(record(aux, MOE_STAGE_STATS, st));
   MOE_TRY(launch_stats(counts, lse, logits, T, N, k, cfg->score_fn, f, P, scalars,
                        at<char>(ws, L.stats), st));
-  record(aux, MOE_N_STAGES, st);
+  MOE_TRY(record(aux, MOE_N_STAGES, st));
   return MOE_OK;
 }
 
