@@ -47,6 +47,7 @@ CASES = [
     (300, 2048, 256, BF16, F32),    # 2 token tiles (ragged), 16 K splits
     (1037, 7168, 160, BF16, F32),   # 5 token tiles, partial expert tile, V3 width
     (600, 1024, 64, BF16, BF16),    # one bf16 piece
+    (300, 256, 20, BF16, F32),      # N % 16 != 0: a part-padded 16-expert block
     (300, 192, 64, BF16, F32),      # 6 k-steps: one split, logits written directly
     (1, 256, 16, BF16, F32),        # a single token
     (300, 256, 64, F32, F32),       # fp32 activations: fp32 MFMA kernel
