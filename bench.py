@@ -241,8 +241,10 @@ def summarize_profile(d: str, workload: str, commands: dict):
     txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
     with open(txt, "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    # gate/up launches: the SwiGLU instantiation (template argument `true`)
-    gate_up = [k for k in traffic if "ffn" in k and "true" in k[k.find("<"):]]
+    # gate/up launches: the ping-pong gate/up kernel, or a SwiGLU
+    # instantiation (template argument `true`) of the other FFN kernels
+    gate_up = [k for k in traffic if "gate_up" in k
+               or ("ffn" in k and "<" in k and "true" in k[k.find("<"):])]
     if gate_up:
         k = max(gate_up, key=lambda n: avg.get(n, 0.0))
         src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")

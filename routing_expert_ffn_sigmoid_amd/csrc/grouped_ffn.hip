@@ -1044,6 +1044,222 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
   }
 }
 
+// ---------------------------------------------------------------------
+// Gate/up kernel for long K: the 4-stage kernel's tiles, loads and LDS
+// layout with a ping-pong schedule.  The dispatcher places waves w and w + 4
+// of a workgroup on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves
+// 4-7) run half a k-step apart: in every phase (closed by a workgroup
+// barrier) one group reads a whole k-step's fragments from LDS into
+// registers, and issues its part of a later stage's loads, while the other
+// group issues that k-step's 32 MFMAs back to back.  Each SIMD's matrix core
+// is then fed by one wave at a time with no LDS waits between its MFMAs.
+// Used for the gate/up phase when K >= 4096 and K % 128 == 0; with short K
+// (64 k-steps per tile at K = 2048) the half-empty first and last phases of
+// a tile and group 1's unshared epilogue cost more than the schedule gains.
+// ---------------------------------------------------------------------
+constexpr int kPpMinK = 4096;
+
+template <int NMBW>
+__device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                     bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
+                                     bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int grp = wave >> 2;  // 0: reads first; 1: half a k-step later
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int K = wave_uniform(g.K);
+  const int nk = K / kBK4;  // multiple of 4
+
+  // loads exactly as in big4_tile: activation row groups of 16 rows x 64
+  // bytes (XOR of row pairs), weight k-blocks of the gate and the up block
+  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
+  const int rows_needed = (2 * NMBW) * 16;
+  constexpr int NAG = (2 * NMBW + 7) / 8;
+  uint32_t aoff[NAG];
+  bool aact[NAG];
+#pragma unroll
+  for (int p = 0; p < NAG; ++p) {
+    const int row = (p * 8 + wave) * 16 + (lane >> 2);
+    int prow = mrow0 + min(row, mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+    aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
+  }
+  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
+  const uint32_t boff = static_cast<uint32_t>(nt * 128 + wave * 16) * krow_bytes + lane * 16u;
+  const uint32_t bsoff1 = static_cast<uint32_t>(g.up_off) * krow_bytes;
+
+  // cnt counts this wave's vector-memory instructions; mark[b] is cnt right
+  // after the loads of the stage in buffer b, so waiting for that stage is
+  // vmcnt(cnt - mark[b])
+  int cnt = 0;
+  int mark[kStages] = {0, 0, 0, 0};
+  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
+    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
+#pragma unroll
+    for (int p = 0; p < NAG; ++p)
+      if (aact[p]) {
+        dma16(ra, aoff[p], kb, Ab + (p * 8 + wave) * 16 * kBK4);
+        ++cnt;
+      }
+    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
+    dma16(rb, boff, kw, Bb + wave * kTileElems);
+    dma16(rb, boff, bsoff1 + kw, Bb + (8 + wave) * kTileElems);
+    cnt += 2;
+  };
+  auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
+
+  // a whole k-step's fragments: M-blocks 2j + wm (j < NMBW), weight blocks
+  // of columns 32wn .. 32wn + 31 (gate and up)
+  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
+  const int aoffs = (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
+  bf16x8 af[NMBW], bf[4];
+  auto read = [&](const bf16_t* Ab, const bf16_t* Bb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      bf[nb] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<true>(wn, nb) * kTileElems));
+#pragma unroll
+    for (int j = 0; j < NMBW; ++j)
+      af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ab + aoffs + j * 32 * kBK4));
+  };
+
+  f32x4 acc[NMBW][4];
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&]() {
+#pragma unroll
+    for (int j = 0; j < NMBW; ++j)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
+  };
+
+  issue(0, A0, B0);
+  mark[0] = cnt;
+  issue(1, A1, B1);
+  mark[1] = cnt;
+  issue(2, A2, B2);
+  mark[2] = cnt;
+  issue(3, A3, B3);
+  mark[3] = cnt;
+  wait_stage(0);
+  __builtin_amdgcn_s_barrier();
+  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
+  __builtin_amdgcn_sched_barrier(0);
+  // k-step k reads stage k (buffer k % 4): group 0 in phase 2k, group 1 in
+  // phase 2k + 1; each computes it in the phase after.  At the start of its
+  // read phase a wave issues its part of stage k + 3 (k >= 1) into buffer
+  // (k + 3) % 4, which last held k-step k - 1, read by both groups by phase
+  // 2k - 1.  Before the barrier that closes phase 2k + 1 every wave waits
+  // for its own loads of stage k + 1, which group 0 reads in phase 2k + 2;
+  // the LDS reads of a read phase are complete (lgkmcnt 0) before its
+  // barrier.
+#define PP_STEP(I, AR, BR, AI, BI)              \
+  {                                             \
+    const int k = st + (I);                     \
+    if (k >= 1 && k + 3 < nk) {                 \
+      issue(k + 3, AI, BI);                     \
+      mark[((I) + 3) % 4] = cnt;                \
+    }                                           \
+    read(AR, BR);                               \
+    wait_lgkmcnt0();                            \
+    if (grp) wait_stage(((I) + 1) % 4);         \
+    __builtin_amdgcn_sched_barrier(0);          \
+    __builtin_amdgcn_s_barrier();               \
+    __builtin_amdgcn_sched_barrier(0);          \
+    compute();                                  \
+    if (!grp) wait_stage(((I) + 1) % 4);        \
+    __builtin_amdgcn_sched_barrier(0);          \
+    __builtin_amdgcn_s_barrier();               \
+    __builtin_amdgcn_sched_barrier(0);          \
+  }
+  for (int st = 0; st < nk; st += kStages) {
+    PP_STEP(0, A0, B0, A3, B3)
+    PP_STEP(1, A1, B1, A0, B0)
+    PP_STEP(2, A2, B2, A1, B1)
+    PP_STEP(3, A3, B3, A2, B2)
+  }
+#undef PP_STEP
+  // group 0 stores its outputs while group 1 runs the last MFMAs; its extra
+  // barrier pairs with group 1's last one, so both groups pass the same
+  // number of barriers per tile.  No LDS is read after that barrier, so the
+  // next tile's loads may start without another one.
+  big_epilogue<sizeof(acc) / sizeof(acc[0]), true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+  if (!grp) __builtin_amdgcn_s_barrier();
+}
+
+// pp_tile for the instantiated height covering nmbw M-blocks per wave
+template <int N>
+__device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, int nt, int mrow0,
+                                            int mv, bf16_t* A0, bf16_t* A1, bf16_t* A2,
+                                            bf16_t* A3, bf16_t* B0, bf16_t* B1, bf16_t* B2,
+                                            bf16_t* B3) {
+  if constexpr (N > 1) {
+    if (nmbw >= N) {
+      pp_tile<N>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+      return;
+    }
+    pp_dispatch<N - 1>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  } else {
+    pp_tile<1>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  }
+}
+
+// Persistent gate/up kernel over the tiles of both groups, in the order of
+// the 4-stage kernel (rounds of gridDim.x tiles, XCD runs, tile_nm).
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_gate_up_pp_kernel(FfnLaunch a) {
+  constexpr int ROWS = kBig4RowsGateUp;
+  __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
+  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
+  if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
+  else build_tile_starts_idle();
+  const int total = tstart[nsegT];
+  const int nxcd = 8;
+  const int per = gridDim.x / nxcd;
+  const int xcd = blockIdx.x % nxcd;
+  const int slot = blockIdx.x / nxcd;
+  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
+    int i0 = 0, i1 = nsegT;
+    while (i1 - i0 > 1) {
+      const int mid = (i0 + i1) >> 1;
+      if (tstart[mid] <= L) i0 = mid;
+      else i1 = mid;
+    }
+    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+    const FfnGroup g = grp ? a.g[1] : a.g[0];
+    const int s = grp ? i0 - a.g[0].nseg : i0;
+    const int r0 = seg_begin(g, s);
+    const int rows = seg_end(g, s) - r0;
+    const int mtc = (rows + ROWS - 1) / ROWS;
+    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
+    const int local = L - tstart[i0];
+    int nt, mt;
+    tile_nm(local, mtc, grp ? a.nt[1] : a.nt[0], nt, mt);
+    const int mrow0 = r0 + mt * rpt;
+    const int mv = min(rpt, rows - mt * rpt);
+    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
+    pp_dispatch<ROWS / 32>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  }
+}
+
 static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st);
 
 static int device_cus() {
@@ -1091,18 +1307,27 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   const long long ub8 = (ub + 7) / 8 * 8;
   if (grid > ub8) grid = ub8;
   grid = (grid + 7) / 8 * 8;
-  bool k128 = true;  // the 4-stage kernel consumes 4 k-steps of 32 per iteration
+  bool k128 = true;  // the 4-stage kernels consume 4 k-steps of 32 per iteration
   bool klong = true;
+  bool kpp = true;
   for (int i = 0; i < fl.ngroups; ++i) {
     k128 = k128 && fl.g[i].K % 128 == 0;
     klong = klong && fl.g[i].K >= 2048;
+    kpp = kpp && fl.g[i].K >= kPpMinK;
+  }
+#ifndef MOE_FFN_NO_BIG4
+  // measured on the V3-shaped prefill layer (K = 7168): the ping-pong
+  // kernel 1.7 % faster than the 4-stage one on gate/up; on v1 (K = 2048)
+  // 2-3 % slower
+  if (phase == 0 && k128 && kpp) {
+    ffn_gate_up_pp_kernel<<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    return hipGetLastError();
   }
   // measured: the 4-stage pipeline wins on the gate/up phase (K = hidden)
   // and on a down phase with K >= 2048 (V3: 2.84 -> 2.73 ms); with shorter K
   // (v1, K = 1408: 44 k-steps per tile) the persistent 2-stage kernel, which
   // overlaps a tile's first loads with the previous tile, is faster
   k128 = k128 && (phase == 0 || klong);
-#ifndef MOE_FFN_NO_BIG4
   if (k128) {
     if (phase == 0)
       ffn_big4_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);

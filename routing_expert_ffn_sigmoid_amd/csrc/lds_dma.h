@@ -41,6 +41,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
                                            wave_uniform(soffset), 0, 0);
 }
 
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned (vmcnt
+// and expcnt unconstrained; gfx9 encoding)
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
 // s_waitcnt with vmcnt <= n, expcnt and lgkmcnt unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
