@@ -286,7 +286,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__
               const float u0 = acc[mb][nb + 2][2 * h], u1 = acc[mb][nb + 2][2 * h + 1];
               const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
               const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-              w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+              w[h] = pack_bf16x2(h0, h1);
             }
             *reinterpret_cast<u32x2*>(orow + col) = u32x2{w[0], w[1]};
           }
@@ -296,10 +296,8 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& c, bf16_t* __restrict__
         for (int nb = 0; nb < 4; ++nb) {
           const int col = c.nt * 256 + wave * 64 + nb * 16 + cq;
           if (col < g.n_out) {
-            const uint32_t w0 = f32_to_bf16(acc[mb][nb][0]) |
-                                (static_cast<uint32_t>(f32_to_bf16(acc[mb][nb][1])) << 16);
-            const uint32_t w1 = f32_to_bf16(acc[mb][nb][2]) |
-                                (static_cast<uint32_t>(f32_to_bf16(acc[mb][nb][3])) << 16);
+            const uint32_t w0 = pack_bf16x2(acc[mb][nb][0], acc[mb][nb][1]);
+            const uint32_t w1 = pack_bf16x2(acc[mb][nb][2], acc[mb][nb][3]);
             *reinterpret_cast<u32x2*>(orow + col) = u32x2{w0, w1};
           }
         }
@@ -490,7 +488,7 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
                 const float u0 = acc[j][nb + 2][2 * h], u1 = acc[j][nb + 2][2 * h + 1];
                 const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
                 const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-                w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+                w[h] = pack_bf16x2(h0, h1);
               }
               *reinterpret_cast<u32x2*>(orow + col) = u32x2{w[0], w[1]};
             }
@@ -500,14 +498,91 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
           for (int nb = 0; nb < 4; ++nb) {
             const int col = nt * 256 + wn * 64 + nb * 16 + cq;
             if (col < g.n_out) {
-              const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
-                                  (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
-              const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
-                                  (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
+              const uint32_t w0 = pack_bf16x2(acc[j][nb][0], acc[j][nb][1]);
+              const uint32_t w1 = pack_bf16x2(acc[j][nb][2], acc[j][nb][3]);
               *reinterpret_cast<u32x2*>(orow + col) = u32x2{w0, w1};
             }
           }
         }
+      }
+    }
+  }
+}
+
+// SwiGLU of a gate/up accumulator pair, rounded to bf16 and packed: two h
+// columns per 32-bit word (lower column in the low half)
+__device__ __forceinline__ uint32_t swiglu_pack(float g0, float g1, float u0, float u1) {
+  const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+  const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+  return pack_bf16x2(h0, h1);
+}
+
+// Tile epilogue through LDS, so the outputs leave as whole rows.  Pass p
+// covers M-block p of both wave rows (tile rows 32p .. 32p + 31): every wave
+// writes its accumulators for those rows, rounded to bf16 (SwiGLU applied in
+// the gate/up phase), into a staging buffer; after a barrier each wave reads
+// whole 1 KiB pieces of the buffer and stores them, so a store instruction
+// writes complete 128-byte lines (two 512-byte rows of a 256-column tile or
+// four 256-byte rows of a 128-column h tile) instead of 32-byte pieces of 16
+// rows, a quarter of the write requests.  The 16-byte chunk c of staged row
+// r sits at position c ^ (r % chunks per row), so the 8-byte writes of 16
+// rows and the row reads touch distinct LDS banks.  The two staging buffers
+// (16 KiB each, free when this is called) alternate, so one barrier per
+// pass orders the writes before the reads, and the reads of pass p before
+// the writes of pass p + 2 (each wave's reads complete before its stores
+// issue, which precede its arrival at the next barrier).  Rows past mv and
+// columns past n_out are not stored (n_out is a multiple of 8).
+template <int NJ, bool SWIGLU>
+__device__ __forceinline__ void staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
+                                                int nmbw, int wm, int wn, int nt, int mrow0,
+                                                int mv, bf16_t* S0, bf16_t* S1) {
+  constexpr int COLS = SWIGLU ? 128 : 256;  // output columns of a tile
+  constexpr int RB = COLS * 2;              // bytes of a staged row
+  constexpr int CPR = RB / 16;              // 16-byte chunks per staged row
+  constexpr int NI = 32 * RB / 1024;        // 1 KiB pieces per pass
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(static_cast<int>(threadIdx.x >> 6));
+  const int rloc = wm * 16 + (lane & 15);   // staged row of this lane's accumulators
+  const int q = lane >> 4;                  // 4-column group inside a 16-column block
+  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+#pragma unroll
+  for (int p = 0; p < NJ; ++p) {
+    if (p < nmbw) {  // tile-uniform
+      char* S = reinterpret_cast<char*>(p & 1 ? S1 : S0);
+      char* srow = S + rloc * RB;
+      if (SWIGLU) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = wn * 32 + nb * 16 + q * 4;
+          const uint32_t w0 = swiglu_pack(acc[p][nb][0], acc[p][nb][1], acc[p][nb + 2][0],
+                                          acc[p][nb + 2][1]);
+          const uint32_t w1 = swiglu_pack(acc[p][nb][2], acc[p][nb][3], acc[p][nb + 2][2],
+                                          acc[p][nb + 2][3]);
+          *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
+              u32x2{w0, w1};
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = wn * 64 + nb * 16 + q * 4;
+          const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
+          const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
+          *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
+              u32x2{w0, w1};
+        }
+      }
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int i0 = 0; i0 < NI; i0 += 8) {
+        const int off = (i0 + wave) * 1024 + lane * 16;
+        const int r = off / RB;
+        const int c = (off % RB) >> 4;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(S + r * RB + ((c ^ (r % CPR)) << 4));
+        const int row = 32 * p + r;
+        const int col = nt * COLS + c * 8;
+        if (row < mv && col < g.n_out)
+          *reinterpret_cast<u32x4*>(Out + static_cast<int64_t>(mrow0 + row) * g.ldo + col) = v;
       }
     }
   }
@@ -675,7 +750,7 @@ __device__ __forceinline__ int big_store(const FfnGroup& g, const f32x4 (&acc)[8
           const float u0 = acc[j][nb + 2][2 * h], u1 = acc[j][nb + 2][2 * h + 1];
           const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
           const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-          w[h] = f32_to_bf16(h0) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
+          w[h] = pack_bf16x2(h0, h1);
         }
         const uint32_t off = (rv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, ro, off, 0, 0);
@@ -684,10 +759,8 @@ __device__ __forceinline__ int big_store(const FfnGroup& g, const f32x4 (&acc)[8
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int col = nt * 256 + wn * 64 + nb * 16 + cq;
-        const uint32_t w0 = f32_to_bf16(acc[j][nb][0]) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][1])) << 16);
-        const uint32_t w1 = f32_to_bf16(acc[j][nb][2]) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc[j][nb][3])) << 16);
+        const uint32_t w0 = pack_bf16x2(acc[j][nb][0], acc[j][nb][1]);
+        const uint32_t w1 = pack_bf16x2(acc[j][nb][2], acc[j][nb][3]);
         const uint32_t off = (rv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off, 0, 0);
       }
@@ -784,12 +857,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
 constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
-// Activation rows per tile of the 4-stage kernel (a multiple of 32, at most
-// 384), per phase.  Taller tiles keep an expert slightly over 256 rows in
-// one tile and load its weights once; measured on the V3-shaped layers, 320
-// rows are 2-4 % faster than 256 on the down phase (K = 2048) but 6 % slower
-// on gate/up (K = 7168, where the taller tile's longer register-bound steps
-// cost more than the saved weight loads).
+// Activation rows per tile of the 4-stage and ping-pong kernels (a multiple
+// of 32, at most 384), per phase.  Taller tiles keep an expert slightly over
+// 256 rows in one tile and load its weights once; measured on the V3-shaped
+// layers, 320 rows are 2-4 % faster than 256 on the down phase (K = 2048)
+// but 6 % slower on gate/up (K = 7168, where the taller tile's longer
+// register-bound steps cost more than the saved weight loads).
 constexpr int kBig4RowsGateUp = 256;
 constexpr int kBig4RowsDown = 320;
 
@@ -1045,21 +1118,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
 }
 
 // ---------------------------------------------------------------------
-// Gate/up kernel for long K: the 4-stage kernel's tiles, loads and LDS
-// layout with a ping-pong schedule.  The dispatcher places waves w and w + 4
-// of a workgroup on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves
-// 4-7) run half a k-step apart: in every phase (closed by a workgroup
-// barrier) one group reads a whole k-step's fragments from LDS into
-// registers, and issues its part of a later stage's loads, while the other
-// group issues that k-step's 32 MFMAs back to back.  Each SIMD's matrix core
-// is then fed by one wave at a time with no LDS waits between its MFMAs.
-// Used for the gate/up phase when K >= 4096 and K % 128 == 0; with short K
-// (64 k-steps per tile at K = 2048) the half-empty first and last phases of
-// a tile and group 1's unshared epilogue cost more than the schedule gains.
+// Ping-pong kernel: the 4-stage kernel's tiles, loads and LDS layout with
+// another schedule.  The dispatcher places waves w and w + 4 of a workgroup
+// on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) run half a
+// k-step apart: in every phase (closed by a workgroup barrier) one group
+// reads a whole k-step's fragments from LDS into registers, and issues its
+// part of a later stage's loads, while the other group issues that k-step's
+// MFMAs back to back.  Each SIMD's matrix core is then fed by one wave at a
+// time with no LDS waits between its MFMAs.
+// Used for the gate/up phase when K >= 4096 and for the down phase when
+// K >= 2048 (K % 128 = 0 both); gate/up with shorter K (v1: 64 k-steps per
+// tile) runs 2 % faster on the 4-stage kernel.  Gate/up tiles store h
+// straight from registers, group 0 while group 1 runs the last MFMAs; down
+// tiles (256 output columns) go through the staged epilogue.
 // ---------------------------------------------------------------------
 constexpr int kPpMinK = 4096;
 
-template <int NMBW>
+template <int NMBW, bool SWIGLU>
 __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
                                      bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
                                      bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3) {
@@ -1091,8 +1166,8 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
   }
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const uint32_t boff = static_cast<uint32_t>(nt * 128 + wave * 16) * krow_bytes + lane * 16u;
-  const uint32_t bsoff1 = static_cast<uint32_t>(g.up_off) * krow_bytes;
+  const uint32_t boff = static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
+  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
 
   // cnt counts this wave's vector-memory instructions; mark[b] is cnt right
   // after the loads of the stage in buffer b, so waiting for that stage is
@@ -1123,7 +1198,7 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       bf[nb] = as_bf16x8(
-          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<true>(wn, nb) * kTileElems));
+          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<SWIGLU>(wn, nb) * kTileElems));
 #pragma unroll
     for (int j = 0; j < NMBW; ++j)
       af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ab + aoffs + j * 32 * kBK4));
@@ -1188,35 +1263,45 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     PP_STEP(3, A3, B3, A2, B2)
   }
 #undef PP_STEP
-  // group 0 stores its outputs while group 1 runs the last MFMAs; its extra
-  // barrier pairs with group 1's last one, so both groups pass the same
-  // number of barriers per tile.  No LDS is read after that barrier, so the
-  // next tile's loads may start without another one.
-  big_epilogue<sizeof(acc) / sizeof(acc[0]), true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
-  if (!grp) __builtin_amdgcn_s_barrier();
+  // Group 0's extra barrier pairs with group 1's last one, so both groups
+  // pass the same number of barriers per tile.
+  if (SWIGLU) {
+    // group 0 stores h while group 1 runs the last MFMAs; no LDS is read
+    // after the extra barrier, so the next tile's loads need no other one
+    big_epilogue<sizeof(acc) / sizeof(acc[0]), true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+    if (!grp) __builtin_amdgcn_s_barrier();
+  } else {
+    // staging in B1/B2: the last k-steps read buffers 3, 0 (group 1 up to
+    // phase 2nk - 1), and no load into B1/B2 is pending
+    if (!grp) __builtin_amdgcn_s_barrier();
+    staged_epilogue<sizeof(acc) / sizeof(acc[0]), false>(g, acc, NMBW, wm, wn, nt, mrow0, mv,
+                                                         B1, B2);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();  // staging reads done before the next tile's loads
+  }
 }
 
 // pp_tile for the instantiated height covering nmbw M-blocks per wave
-template <int N>
+template <int N, bool SWIGLU>
 __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, int nt, int mrow0,
                                             int mv, bf16_t* A0, bf16_t* A1, bf16_t* A2,
                                             bf16_t* A3, bf16_t* B0, bf16_t* B1, bf16_t* B2,
                                             bf16_t* B3) {
   if constexpr (N > 1) {
     if (nmbw >= N) {
-      pp_tile<N>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+      pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
       return;
     }
-    pp_dispatch<N - 1>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    pp_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
   } else {
-    pp_tile<1>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
   }
 }
 
-// Persistent gate/up kernel over the tiles of both groups, in the order of
+// Persistent ping-pong kernel over the tiles of both groups, in the order of
 // the 4-stage kernel (rounds of gridDim.x tiles, XCD runs, tile_nm).
-__global__ __launch_bounds__(kBigThreads, 1) void ffn_gate_up_pp_kernel(FfnLaunch a) {
-  constexpr int ROWS = kBig4RowsGateUp;
+template <bool SWIGLU, int ROWS>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
   __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
   __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
@@ -1256,7 +1341,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_gate_up_pp_kernel(FfnLaunc
     const int mrow0 = r0 + mt * rpt;
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
-    pp_dispatch<ROWS / 32>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    pp_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
   }
 }
 
@@ -1316,23 +1401,25 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
     kpp = kpp && fl.g[i].K >= kPpMinK;
   }
 #ifndef MOE_FFN_NO_BIG4
-  // measured on the V3-shaped prefill layer (K = 7168): the ping-pong
-  // kernel 1.7 % faster than the 4-stage one on gate/up; on v1 (K = 2048)
-  // 2-3 % slower
-  if (phase == 0 && k128 && kpp) {
-    ffn_gate_up_pp_kernel<<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+  // Measured choices (V3 prefill: gate/up K = 7168, down K = 2048; v1 and
+  // v2: gate/up K = 2048, down K = 1408):
+  //  - gate/up, K >= 4096: ping-pong kernel, 1.2-1.7 % faster than the
+  //    4-stage kernel; at K = 2048 2 % slower, so shorter K keeps the latter;
+  //  - down, K >= 2048: ping-pong kernel with 320-row tiles and the staged
+  //    epilogue, 2.6-3.2 % faster than the 4-stage kernel (which was 4 %
+  //    faster than the 2-stage one);
+  //  - down with shorter K (44 k-steps per tile at 1408): the persistent
+  //    2-stage kernel, which overlaps a tile's first loads with the previous
+  //    tile, is faster.
+  if (k128 && phase == 0) {
+    if (kpp)
+      ffn_pp_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+    else
+      ffn_big4_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
-  // measured: the 4-stage pipeline wins on the gate/up phase (K = hidden)
-  // and on a down phase with K >= 2048 (V3: 2.84 -> 2.73 ms); with shorter K
-  // (v1, K = 1408: 44 k-steps per tile) the persistent 2-stage kernel, which
-  // overlaps a tile's first loads with the previous tile, is faster
-  k128 = k128 && (phase == 0 || klong);
-  if (k128) {
-    if (phase == 0)
-      ffn_big4_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
-    else
-      ffn_big4_kernel<false, kBig4RowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+  if (k128 && klong) {
+    ffn_pp_kernel<false, kBig4RowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
 #endif

@@ -175,15 +175,15 @@ def test_bf16_small_layer_parity_and_determinism():
 
 @pytest.mark.parametrize("rows_per_seg,inter,H", [(5, 192, 256), (40, 192, 256), (150, 192, 256),
                                                    (400, 192, 256), (150, 2048, 256),
-                                                   (400, 2048, 256), (150, 256, 4096),
-                                                   (300, 128, 4096)])
+                                                   (400, 2048, 256), (150, 2048, 448),
+                                                   (150, 256, 4096), (300, 128, 4096)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
-    """moe_grouped_ffn alone: ragged and empty segments, every tile height;
-    an expert width of 2048 sends the down projection of large segments
-    through the 4-stage kernel (K >= 2048), 192 through the 2-stage one; a
-    hidden size of 4096 sends the gate/up projection of large segments
-    through the ping-pong kernel (K >= 4096).  At H = 4096 every row of the
-    multi-tile segment and every 4th row of the others is compared."""
+    """moe_grouped_ffn alone: ragged and empty segments, every tile height.
+    Large segments: an expert width of 2048 sends the down projection
+    through the ping-pong kernel (K >= 2048; with H = 448 its second column
+    tile is partial), 192 through the 2-stage one; a hidden size of 4096
+    sends the gate/up projection through the ping-pong kernel (K >= 4096),
+    256 through the 4-stage one."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
     nseg = 9
@@ -207,11 +207,11 @@ def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     torch.cuda.synchronize()
     an = typed(a)
     w13n, w2n = typed(w13), typed(w2)
-    rows = [r_ for s in range(nseg) for r_ in range(offs[s], offs[s + 1])
-            if H < 4096 or s == 5 or r_ % 4 == 0]
-    seg_of = np.searchsorted(offs, np.arange(M), side="right") - 1
-    ref = np.stack([oracle.swiglu_row(an[r_], w13n[seg_of[r_]], w2n[seg_of[r_]]) for r_ in rows])
-    mr, l2 = normwise(f64(y)[rows], ref)
+    ref = np.empty((M, H))
+    for s in range(nseg):
+        for r_ in range(offs[s], offs[s + 1]):
+            ref[r_] = oracle.swiglu_row(an[r_], w13n[s], w2n[s])
+    mr, l2 = normwise(f64(y), ref)
     say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
     assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
 
