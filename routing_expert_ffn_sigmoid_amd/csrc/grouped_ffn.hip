@@ -1134,6 +1134,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
 // ---------------------------------------------------------------------
 constexpr int kPpMinK = 4096;
 
+// s_waitcnt allowing N stages of a wave's loads to stay outstanding, a stage
+// being OPS0 loads, or OPS0 + 1 on waves with `extra` set; N < 0: no wait
+template <int OPS0, int N>
+__device__ __forceinline__ void pp_wait_stages(bool extra) {
+  if constexpr (N >= 0) {
+    if (extra) wait_vmcnt<N * (OPS0 + 1)>();
+    else wait_vmcnt<N * OPS0>();
+  }
+}
+
 template <int NMBW, bool SWIGLU>
 __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
                                      bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
@@ -1188,6 +1198,15 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     cnt += 2;
   };
   auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
+  // Per stage every wave issues 2 weight loads and G / 8 activation groups,
+  // one more on the first G % 8 waves (G = 2 * NMBW groups of 16 rows dealt
+  // round-robin), so "at most n stages outstanding" is a constant vmcnt
+  // picked by one wave-uniform branch.  The run-time wait above (a tree of
+  // scalar branches) cost 11 % of a compute-only down launch; tiles of 9 or
+  // 10 M-blocks keep it, since with constant waits the compiler spills
+  // their registers.
+  constexpr int G = 2 * NMBW;
+  const bool extra = wave < (G % 8);
 
   // a whole k-step's fragments: M-blocks 2j + wm (j < NMBW), weight blocks
   // of columns 32wn .. 32wn + 31 (gate and up)
@@ -1235,8 +1254,16 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   // (k + 3) % 4, which last held k-step k - 1, read by both groups by phase
   // 2k - 1.  Before the barrier that closes phase 2k + 1 every wave waits
   // for its own loads of stage k + 1, which group 0 reads in phase 2k + 2;
-  // the LDS reads of a read phase are complete (lgkmcnt 0) before its
-  // barrier.
+  // after them stages k + 2 and k + 3 may be outstanding, in the last four
+  // k-steps fewer.  The LDS reads of a read phase are complete (lgkmcnt 0)
+  // before its barrier.
+#define PP_WAIT(I)                                                   \
+  if constexpr (NMBW > 8) {                                          \
+    wait_stage(((I) + 1) % 4);                                       \
+  } else {                                                           \
+    if (last) pp_wait_stages<2 + G / 8, 2 - (I)>(extra);             \
+    else pp_wait_stages<2 + G / 8, 2>(extra);                        \
+  }
 #define PP_STEP(I, AR, BR, AI, BI)              \
   {                                             \
     const int k = st + (I);                     \
@@ -1246,23 +1273,25 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     }                                           \
     read(AR, BR);                               \
     wait_lgkmcnt0();                            \
-    if (grp) wait_stage(((I) + 1) % 4);         \
+    if (grp) { PP_WAIT(I) }                     \
     __builtin_amdgcn_sched_barrier(0);          \
     __builtin_amdgcn_s_barrier();               \
     __builtin_amdgcn_sched_barrier(0);          \
     compute();                                  \
-    if (!grp) wait_stage(((I) + 1) % 4);        \
+    if (!grp) { PP_WAIT(I) }                    \
     __builtin_amdgcn_sched_barrier(0);          \
     __builtin_amdgcn_s_barrier();               \
     __builtin_amdgcn_sched_barrier(0);          \
   }
   for (int st = 0; st < nk; st += kStages) {
+    const bool last = st + kStages >= nk;  // the last four k-steps
     PP_STEP(0, A0, B0, A3, B3)
     PP_STEP(1, A1, B1, A0, B0)
     PP_STEP(2, A2, B2, A1, B1)
     PP_STEP(3, A3, B3, A2, B2)
   }
 #undef PP_STEP
+#undef PP_WAIT
   // Group 0's extra barrier pairs with group 1's last one, so both groups
   // pass the same number of barriers per tile.
   if (SWIGLU) {
