@@ -843,296 +843,31 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 }
 
 // ---------------------------------------------------------------------
-// 4-stage variant (k-steps of 32), four LDS buffers of both operands.  The
-// workgroup barrier closes each step: before it every wave waits for its
-// own loads of the stage after next (s_waitcnt vmcnt), so after it that
-// stage is in LDS for all waves, and the buffer the finished step read is
-// free for the stage four steps ahead (two steps of load latency are then
-// covered).  Because the next stage is already visible during a step, the
-// step's last M-blocks also read the next step's first fragments (four
-// weight, two activation), and the MFMAs after the barrier start without
-// waiting on LDS.  A tile ends with that barrier, so the next tile may load
-// all four buffers at once.  Used when K is a multiple of 128.
+// Ping-pong kernel (large segments, K % 128 = 0: both phases of the
+// V3-shaped prefill layers, the gate/up phase of v1/v2).  Tiles of up to
+// kTileRows* activation rows x 256 weight rows, k-steps of 32, four LDS
+// stages of both operands filled by direct global->LDS loads.
+// The dispatcher places waves w and w + 4 of a workgroup on the same SIMD.
+// Group 0 (waves 0-3) and group 1 (waves 4-7) run half a k-step apart: in
+// every phase (closed by a workgroup barrier) one group reads a whole
+// k-step's fragments from LDS into registers, and issues its part of a
+// later stage's loads, while the other group issues that k-step's MFMAs
+// back to back.  Each SIMD's matrix core is then fed by one wave at a time
+// with no LDS waits between its MFMAs.  Gate/up tiles store h straight from
+// registers, group 0 while group 1 runs the last MFMAs; down tiles (256
+// output columns) go through the staged epilogue.
 // ---------------------------------------------------------------------
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
 constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
-// Activation rows per tile of the 4-stage and ping-pong kernels (a multiple
-// of 32, at most 384), per phase.  Taller tiles keep an expert slightly over
-// 256 rows in one tile and load its weights once; measured on the V3-shaped
-// layers, 320 rows are 2-4 % faster than 256 on the down phase (K = 2048)
-// but 6 % slower on gate/up (K = 7168, where the taller tile's longer
-// register-bound steps cost more than the saved weight loads).
-constexpr int kBig4RowsGateUp = 256;
-constexpr int kBig4RowsDown = 320;
-
-
-// first fragments of a step: the four weight fragments and the first two
-// activation fragments
-template <int NMBW, bool SWIGLU>
-__device__ __forceinline__ void big4_first(const bf16_t* __restrict__ Ab,
-                                           const bf16_t* __restrict__ Bb, int wm, int wn,
-                                           bf16x8 (&bf)[4], bf16x8 (&a01)[2]) {
-  const int lane = threadIdx.x & 63;
-  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
-  const bf16_t* abase = Ab + (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
-  const bf16_t* bbase = Bb + lane * 8;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    bf[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(bbase + big_wblock<SWIGLU>(wn, nb) * kTileElems));
-  a01[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase));
-  a01[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (NMBW > 1 ? 32 * kBK4 : 0)));
-}
-
-// One k-step from (bf, a01) and the rest of buffer Ab; during the last two
-// M-blocks the next step's first fragments are read from (An, Bn) into
-// (bf, a01), so the MFMAs after the next barrier start at once.
-template <int NMBW, bool SWIGLU>
-__device__ __forceinline__ void big4_step(const bf16_t* __restrict__ Ab,
-                                          const bf16_t* __restrict__ An,
-                                          const bf16_t* __restrict__ Bn,
-                                          f32x4 (&acc)[NMBW][4], int wm, int wn,
-                                          bf16x8 (&bf)[4], bf16x8 (&a01)[2]) {
-  const int lane = threadIdx.x & 63;
-  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
-  const int aoffs = (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
-  const bf16_t* abase = Ab + aoffs;
-  const bf16_t* anext = An + aoffs;
-  const bf16_t* bnext = Bn + lane * 8;
-  bf16x8 af[NMBW];
-  af[0] = a01[0];
-  if (NMBW > 1) af[1] = a01[1];
-  bf16x8 nbf[4], na[2];
-  constexpr int J0 = NMBW >= 2 ? NMBW - 2 : 0;
-#pragma unroll
-  for (int j = 0; j < NMBW; ++j) {
-    if (j + 2 < NMBW)
-      af[j + 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (j + 2) * 32 * kBK4));
-    if (j == J0) {
-      nbf[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 0) * kTileElems));
-      nbf[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 1) * kTileElems));
-      nbf[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 2) * kTileElems));
-    }
-    if (j == NMBW - 1) {
-      nbf[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(bnext + big_wblock<SWIGLU>(wn, 3) * kTileElems));
-      na[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(anext));
-      na[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(anext + (NMBW > 1 ? 32 * kBK4 : 0)));
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
-  }
-  // issue order: per M-block 2 MFMAs, the block's LDS reads, 2 MFMAs
-#pragma unroll
-  for (int j = 0; j < NMBW; ++j) {
-    const int nreads = (j + 2 < NMBW ? 1 : 0) + (j == J0 ? 3 : 0) + (j == NMBW - 1 ? 3 : 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    switch (nreads) {
-      case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
-      case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
-      case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
-      case 6: __builtin_amdgcn_sched_group_barrier(0x100, 6, 0); break;
-      case 7: __builtin_amdgcn_sched_group_barrier(0x100, 7, 0); break;
-      default: break;
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  }
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) bf[nb] = nbf[nb];
-  a01[0] = na[0];
-  a01[1] = na[1];
-}
-template <int NMBW, bool SWIGLU>
-__device__ __noinline__ void big4_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                       bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
-                                       bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int K = wave_uniform(g.K);
-  const int nk = K / kBK4;  // multiple of 4
-
-  // DMA geometry: 16 rows x 64 bytes per wave instruction; row group
-  // q = p*8 + wave covers tile rows [16q, 16q+16); lane -> row 16q + lane/4,
-  // physical chunk lane%4, logical chunk (lane%4) ^ ((row >> 1) & 3), and
-  // (row >> 1) & 3 = (lane >> 3) & 3 for every q.  (With 64-byte rows this
-  // XOR of row pairs is the pattern that keeps 16-byte fragment reads free
-  // of bank conflicts on gfx950; XOR by row quads is not.)
-  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
-  const int rows_needed = (2 * NMBW) * 16;
-  constexpr int NAG = (2 * NMBW + 7) / 8;  // activation row groups of 16 per wave (at most)
-  uint32_t aoff[NAG];
-  bool aact[NAG];
-#pragma unroll
-  for (int p = 0; p < NAG; ++p) {
-    const int row = (p * 8 + wave) * 16 + (lane >> 2);
-    int prow = mrow0 + min(row, mv - 1);
-    if (g.row_index) prow = g.row_index[prow];
-    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
-    aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
-  }
-  // weights, tiled: the wave copies the KiB of k-block `step` of row blocks
-  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
-  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order
-  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const int col0 = SWIGLU ? nt * 128 : nt * 256;
-  const uint32_t boff = static_cast<uint32_t>(col0 + wave * 16) * krow_bytes + lane * 16u;
-  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
-
-  // Every vector-memory instruction this wave issues in the tile is counted
-  // (cnt); mark[b] is cnt right after stage b's loads.  Waiting for stage b
-  // = s_waitcnt vmcnt(cnt - mark[b]): vmcnt retires in issue order.
-  int cnt = 0;
-  int mark[kStages] = {0, 0, 0, 0};
-  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
-    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
-#pragma unroll
-    for (int p = 0; p < NAG; ++p)
-      if (aact[p]) {
-        dma16(ra, aoff[p], kb, Ab + (p * 8 + wave) * 16 * kBK4);
-        ++cnt;
-      }
-    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
-    dma16(rb, boff, kw, Bb + (0 * 8 + wave) * kTileElems);
-    dma16(rb, boff, bsoff1 + kw, Bb + (1 * 8 + wave) * kTileElems);
-    cnt += 2;
-  };
-  auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
-
-  f32x4 acc[NMBW][4];
-#pragma unroll
-  for (int j = 0; j < NMBW; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // the barrier closes each step: after it, the next stage (waited for
-  // before it) is visible and the buffer the step read is free for the
-  // stage four steps ahead
-  issue(0, A0, B0);
-  mark[0] = cnt;
-  issue(1, A1, B1);
-  mark[1] = cnt;
-  issue(2, A2, B2);
-  mark[2] = cnt;
-  issue(3, A3, B3);
-  mark[3] = cnt;
-  wait_stage(1);
-  __builtin_amdgcn_s_barrier();
-  bf16x8 bf[4], a01[2];
-  big4_first<NMBW, SWIGLU>(A0, B0, wm, wn, bf, a01);
-  for (int st = 0; st < nk; st += kStages) {
-    big4_step<NMBW, SWIGLU>(A0, A1, B1, acc, wm, wn, bf, a01);
-    wait_stage(2);
-    __builtin_amdgcn_s_barrier();
-    if (st + 4 < nk) issue(st + 4, A0, B0);
-    mark[0] = cnt;
-    big4_step<NMBW, SWIGLU>(A1, A2, B2, acc, wm, wn, bf, a01);
-    wait_stage(3);
-    __builtin_amdgcn_s_barrier();
-    if (st + 5 < nk) issue(st + 5, A1, B1);
-    mark[1] = cnt;
-    big4_step<NMBW, SWIGLU>(A2, A3, B3, acc, wm, wn, bf, a01);
-    wait_stage(0);
-    __builtin_amdgcn_s_barrier();
-    if (st + 6 < nk) issue(st + 6, A2, B2);
-    mark[2] = cnt;
-    big4_step<NMBW, SWIGLU>(A3, A0, B0, acc, wm, wn, bf, a01);
-    wait_stage(1);
-    __builtin_amdgcn_s_barrier();
-    if (st + 7 < nk) issue(st + 7, A3, B3);
-    mark[3] = cnt;
-  }
-  big_epilogue<sizeof(acc) / sizeof(acc[0]), SWIGLU>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
-}
-
-// big4_tile for the instantiated height covering nmbw M-blocks per wave
-template <int N, bool SWIGLU>
-__device__ __forceinline__ void big4_dispatch(int nmbw, const FfnGroup& g, int s, int nt,
-                                              int mrow0, int mv, bf16_t* A0, bf16_t* A1,
-                                              bf16_t* A2, bf16_t* A3, bf16_t* B0, bf16_t* B1,
-                                              bf16_t* B2, bf16_t* B3) {
-  if constexpr (N > 1) {
-    if (nmbw >= N) {
-      big4_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
-      return;
-    }
-    big4_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
-  } else {
-    big4_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
-  }
-}
-
-template <bool SWIGLU, int ROWS>
-__global__ __launch_bounds__(kBigThreads, 1) void ffn_big4_kernel(FfnLaunch a) {
-  static_assert(ROWS % 32 == 0 && ROWS <= 384, "tile rows");
-  __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
-  __shared__ int tstart[kMaxSegs + 1];
-  __shared__ int tmp[kThreads];
-
-  const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
-  if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
-  else build_tile_starts_idle();
-  const int total = tstart[nsegT];
-  const int nxcd = 8;
-  const int per = gridDim.x / nxcd;
-  const int xcd = blockIdx.x % nxcd;
-  const int slot = blockIdx.x / nxcd;
-  // rounds of gridDim.x consecutive tiles; inside a round XCD x takes the
-  // x-th run of `per` tiles (two experts' n-tiles: shared activation rows in
-  // one L2), and every XCD gets work in every round
-  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
-    int i0 = 0, i1 = nsegT;
-    while (i1 - i0 > 1) {
-      const int mid = (i0 + i1) >> 1;
-      if (tstart[mid] <= L) i0 = mid;
-      else i1 = mid;
-    }
-    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
-    const FfnGroup g = grp ? a.g[1] : a.g[0];
-    const int s = grp ? i0 - a.g[0].nseg : i0;
-    const int r0 = seg_begin(g, s);
-    const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + ROWS - 1) / ROWS;
-    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
-    const int local = L - tstart[i0];
-    int nt, mt;
-    tile_nm(local, mtc, grp ? a.nt[1] : a.nt[0], nt, mt);
-    const int mrow0 = r0 + mt * rpt;
-    const int mv = min(rpt, rows - mt * rpt);
-    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
-    big4_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------
-// Ping-pong kernel: the 4-stage kernel's tiles, loads and LDS layout with
-// another schedule.  The dispatcher places waves w and w + 4 of a workgroup
-// on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) run half a
-// k-step apart: in every phase (closed by a workgroup barrier) one group
-// reads a whole k-step's fragments from LDS into registers, and issues its
-// part of a later stage's loads, while the other group issues that k-step's
-// MFMAs back to back.  Each SIMD's matrix core is then fed by one wave at a
-// time with no LDS waits between its MFMAs.
-// Used for the gate/up phase when K >= 4096 and for the down phase when
-// K >= 2048 (K % 128 = 0 both); gate/up with shorter K (v1: 64 k-steps per
-// tile) runs 2 % faster on the 4-stage kernel.  Gate/up tiles store h
-// straight from registers, group 0 while group 1 runs the last MFMAs; down
-// tiles (256 output columns) go through the staged epilogue.
-// ---------------------------------------------------------------------
-constexpr int kPpMinK = 4096;
+// Activation rows per tile (a multiple of 32, at most 384), per phase.
+// Taller tiles keep an expert slightly over 256 rows in one tile and load
+// its weights once; measured on the V3-shaped layers, 320 rows are 4 %
+// faster than 256 on the down phase (K = 2048) but 5 % slower on gate/up
+// (K = 7168: the 9- and 10-block tiles' longer phases and run-time waits
+// cost more than the saved weight loads).
+constexpr int kTileRowsGateUp = 256;
+constexpr int kTileRowsDown = 320;
 
 // s_waitcnt allowing N stages of a wave's loads to stay outstanding, a stage
 // being OPS0 loads, or OPS0 + 1 on waves with `extra` set; N < 0: no wait
@@ -1157,8 +892,14 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   const int K = wave_uniform(g.K);
   const int nk = K / kBK4;  // multiple of 4
 
-  // loads exactly as in big4_tile: activation row groups of 16 rows x 64
-  // bytes (XOR of row pairs), weight k-blocks of the gate and the up block
+  // Activation loads: 16 rows x 64 bytes per wave instruction; row group
+  // q = p*8 + wave covers tile rows [16q, 16q+16); lane -> row 16q + lane/4,
+  // physical chunk lane%4, logical chunk (lane%4) ^ ((row >> 1) & 3), and
+  // (row >> 1) & 3 = (lane >> 3) & 3 for every q.  (With 64-byte rows this
+  // XOR of row pairs keeps the 16-byte fragment reads free of bank
+  // conflicts on gfx950; XOR by row quads does not.)  Rows past the tile's
+  // valid ones repeat its last row; groups past the tile's height are not
+  // loaded.
   const int logical = (lane & 3) ^ ((lane >> 3) & 3);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(
@@ -1175,8 +916,12 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
     aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
   }
+  // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
+  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
+  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const uint32_t boff = static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
+  const uint32_t boff =
+      static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
   const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
 
   // cnt counts this wave's vector-memory instructions; mark[b] is cnt right
@@ -1327,8 +1072,10 @@ __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, 
   }
 }
 
-// Persistent ping-pong kernel over the tiles of both groups, in the order of
-// the 4-stage kernel (rounds of gridDim.x tiles, XCD runs, tile_nm).
+// Persistent ping-pong kernel over the tiles of both groups: rounds of
+// gridDim.x tiles, inside a round XCD x takes the x-th run of gridDim.x / 8
+// tiles (tiles sharing activation rows or weights in one L2), tile_nm order
+// inside a segment.
 template <bool SWIGLU, int ROWS>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
@@ -1421,34 +1168,22 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   const long long ub8 = (ub + 7) / 8 * 8;
   if (grid > ub8) grid = ub8;
   grid = (grid + 7) / 8 * 8;
-  bool k128 = true;  // the 4-stage kernels consume 4 k-steps of 32 per iteration
+  bool k128 = true;  // the ping-pong kernel consumes 4 k-steps of 32 per iteration
   bool klong = true;
-  bool kpp = true;
   for (int i = 0; i < fl.ngroups; ++i) {
     k128 = k128 && fl.g[i].K % 128 == 0;
     klong = klong && fl.g[i].K >= 2048;
-    kpp = kpp && fl.g[i].K >= kPpMinK;
   }
-#ifndef MOE_FFN_NO_BIG4
-  // Measured choices (V3 prefill: gate/up K = 7168, down K = 2048; v1 and
-  // v2: gate/up K = 2048, down K = 1408):
-  //  - gate/up, K >= 4096: ping-pong kernel, 1.2-1.7 % faster than the
-  //    4-stage kernel; at K = 2048 2 % slower, so shorter K keeps the latter;
-  //  - down, K >= 2048: ping-pong kernel with 320-row tiles and the staged
-  //    epilogue, 2.6-3.2 % faster than the 4-stage kernel (which was 4 %
-  //    faster than the 2-stage one);
-  //  - down with shorter K (44 k-steps per tile at 1408): the persistent
-  //    2-stage kernel, which overlaps a tile's first loads with the previous
-  //    tile, is faster.
-  if (k128 && phase == 0) {
-    if (kpp)
-      ffn_pp_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+#ifndef MOE_FFN_NO_PP
+  // Measured (V3 prefill: gate/up K = 7168, down K = 2048; v1 and v2:
+  // gate/up K = 2048, down K = 1408): a down phase with K < 2048 (44
+  // k-steps per tile at 1408) runs faster on the persistent 2-stage kernel,
+  // which overlaps a tile's first loads with the previous tile.
+  if (k128 && (phase == 0 || klong)) {
+    if (phase == 0)
+      ffn_pp_kernel<true, kTileRowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     else
-      ffn_big4_kernel<true, kBig4RowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
-    return hipGetLastError();
-  }
-  if (k128 && klong) {
-    ffn_pp_kernel<false, kBig4RowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+      ffn_pp_kernel<false, kTileRowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
 #endif

@@ -179,11 +179,10 @@ def test_bf16_small_layer_parity_and_determinism():
                                                    (150, 256, 4096), (300, 128, 4096)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height.
-    Large segments: an expert width of 2048 sends the down projection
-    through the ping-pong kernel (K >= 2048; with H = 448 its second column
-    tile is partial), 192 through the 2-stage one; a hidden size of 4096
-    sends the gate/up projection through the ping-pong kernel (K >= 4096),
-    256 through the 4-stage one."""
+    Large segments run the gate/up projection (K = H, a multiple of 128, up
+    to 4096 here) on the ping-pong kernel; an expert width of 2048 sends the
+    down projection there too (K >= 2048; with H = 448 its second column
+    tile is partial), 128-256 through the 2-stage kernel."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
     nseg = 9
