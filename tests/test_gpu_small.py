@@ -176,11 +176,13 @@ def test_bf16_small_layer_parity_and_determinism():
 @pytest.mark.parametrize("rows_per_seg,inter,H", [(5, 192, 256), (40, 192, 256), (150, 192, 256),
                                                    (400, 192, 256), (150, 2048, 256),
                                                    (400, 2048, 256), (150, 2048, 448),
-                                                   (150, 256, 4096), (300, 128, 4096)])
+                                                   (150, 128, 128), (150, 256, 4096),
+                                                   (300, 128, 4096)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height.
-    Large segments run the gate/up projection (K = H, a multiple of 128, up
-    to 4096 here) on the ping-pong kernel; an expert width of 2048 sends the
+    Large segments run the gate/up projection (K = H, a multiple of 128,
+    from 128 = four k-steps, all in the kernel's last loop iteration, up to
+    4096 here) on the ping-pong kernel; an expert width of 2048 sends the
     down projection there too (K >= 2048; with H = 448 its second column
     tile is partial), 128-256 through the 2-stage kernel."""
     require_gpu()
