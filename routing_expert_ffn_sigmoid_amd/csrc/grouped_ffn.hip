@@ -394,7 +394,7 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     case 12: wait_vmcnt<12>(); break;
     case 13: wait_vmcnt<13>(); break;
     case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 2 stages x 5 loads
+    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 3 stages x 5 loads
   }
 }
 
