@@ -864,8 +864,8 @@ constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
 // Taller tiles keep an expert slightly over 256 rows in one tile and load
 // its weights once; measured on the V3-shaped layers, 320 rows are 4 %
 // faster than 256 on the down phase (K = 2048) but 5 % slower on gate/up
-// (K = 7168: the 9- and 10-block tiles' longer phases and run-time waits
-// cost more than the saved weight loads).
+// (K = 7168, 288 rows: 1 % slower; the 9- and 10-block tiles' longer
+// phases cost more than the saved weight loads).
 constexpr int kTileRowsGateUp = 256;
 constexpr int kTileRowsDown = 320;
 
@@ -1078,6 +1078,9 @@ __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, 
 // inside a segment.
 template <bool SWIGLU, int ROWS>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
+  // at most 3 activation row groups of 16 per wave and stage; at most 10
+  // M-blocks per wave fit the register file without spills
+  static_assert(ROWS % 32 == 0 && ROWS <= 320, "tile rows");
   __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
   __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
   __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
