@@ -37,6 +37,10 @@
  *     calls on different streams need their own workspaces.
  *   - Outputs are deterministic: the same inputs give bit-identical outputs
  *     (no floating-point atomics on any output path).
+ *   - A call enqueues only kernel launches (and the requested event records)
+ *     on `stream`; buffers are cleared by kernels, not memset.  Calls can
+ *     therefore be captured into a HIP graph and replayed; each replay
+ *     reproduces the eager call bit for bit.
  */
 #ifndef MOE_H
 #define MOE_H
