@@ -1045,8 +1045,9 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     big_epilogue<sizeof(acc) / sizeof(acc[0]), true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
     if (!grp) __builtin_amdgcn_s_barrier();
   } else {
-    // staging in B1/B2: the last k-steps read buffers 3, 0 (group 1 up to
-    // phase 2nk - 1), and no load into B1/B2 is pending
+    // staging in B1/B2: every read phase ended with lgkmcnt(0) before its
+    // barrier (group 1's last one closes phase 2nk - 1) and every load was
+    // waited for, so both buffers are free
     if (!grp) __builtin_amdgcn_s_barrier();
     staged_epilogue<sizeof(acc) / sizeof(acc[0]), false>(g, acc, NMBW, wm, wn, nt, mrow0, mv,
                                                          B1, B2);
