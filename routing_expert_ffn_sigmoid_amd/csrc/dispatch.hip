@@ -203,36 +203,92 @@ __device__ uint64_t radix_select_key(const uint64_t* __restrict__ keys, int n, i
   __shared__ int hist[256];
   __shared__ unsigned long long sh_prefix;
   __shared__ int sh_need;
+  __shared__ int sh_done;
   if (threadIdx.x == 0) {
     sh_prefix = 0ull;
     sh_need = need;
+    sh_done = 0;
   }
   for (int d = 7; d >= 0; --d) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     const uint64_t prefix = sh_prefix;
     const int hs = 8 * (d + 1);
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint64_t key = keys[i];
-      const bool match = (d == 7) || ((key >> hs) == (prefix >> hs));
-      if (match) atomicAdd(&hist[(key >> (8 * d)) & 255], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int left = sh_need;
-      int cum = 0;
-      int digit = 0;
-      for (int v = 255; v >= 0; --v) {
-        if (cum + hist[v] >= left) {
-          digit = v;
-          break;
-        }
-        cum += hist[v];
+    const int lane = threadIdx.x & 63;
+    // batches of 8 keys per thread, loaded before they are counted, so 8
+    // loads are in flight instead of one (uniform trip count)
+    constexpr int kB = 8;
+    for (int i0 = 0; i0 < n; i0 += kB * static_cast<int>(blockDim.x)) {
+      uint64_t kb[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = i0 + j * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+        kb[j] = i < n ? keys[i] : 0ull;
       }
-      sh_need = left - cum;
-      sh_prefix = prefix | (static_cast<uint64_t>(digit) << (8 * d));
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = i0 + j * static_cast<int>(blockDim.x) + static_cast<int>(threadIdx.x);
+        const uint64_t key = kb[j];
+        const bool match = i < n && ((d == 7) || ((key >> hs) == (prefix >> hs)));
+        const int dg = static_cast<int>((key >> (8 * d)) & 255);
+        // The top digits of one expert's keys (its scores' exponent) fall
+        // into one or two bins: lanes sharing the first pending lane's digit
+        // add their count with one atomic, up to four rounds, the rest one
+        // each.
+        uint64_t act = __ballot(match);
+        for (int it = 0; it < 4 && act != 0ull; ++it) {
+          const int lead = __ffsll(static_cast<unsigned long long>(act)) - 1;
+          const int ld = __shfl(dg, lead);
+          const uint64_t same = __ballot(match && dg == ld) & act;
+          if (lane == lead) atomicAdd(&hist[ld], __popcll(same));
+          act &= ~same;
+        }
+        if ((act >> lane) & 1ull) atomicAdd(&hist[dg], 1);
+      }
     }
     __syncthreads();
+    // The digit whose bin holds the left-th largest matching key: wave 0
+    // takes the bins in descending order, four per lane (lane l: 255 - 4l
+    // down to 252 - 4l), forms the running count over lanes, and the first
+    // lane whose running count reaches `left` finds the digit in its bins.
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const int left = sh_need;  // >= 1 and at most the matching keys
+      int h[4];
+      int own = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = hist[255 - 4 * l - q];
+        own += h[q];
+      }
+      int incl = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (l >= o) incl += t;
+      }
+      const uint64_t reach = __ballot(incl >= left);
+      if (l == __ffsll(static_cast<unsigned long long>(reach)) - 1) {
+        int cum = incl - own;
+        int digit = 252 - 4 * l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (cum + h[q] >= left) {
+            digit = 255 - 4 * l - q;
+            break;
+          }
+          cum += h[q];
+        }
+        sh_need = left - cum;
+        sh_prefix = prefix | (static_cast<uint64_t>(digit) << (8 * d));
+        // every key of the bin is needed: the prefix with zero lower digits
+        // is the threshold (keys are distinct, those below the bin are not
+        // kept)
+        sh_done = (left - cum == hist[digit]) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (sh_done) break;  // uniform
   }
   const uint64_t tau = sh_prefix;
   __syncthreads();
@@ -245,23 +301,38 @@ __device__ void assign_kept_rows(const uint64_t* __restrict__ keys,
                                  const int32_t* __restrict__ slots, int c, uint64_t tau,
                                  int base_row, int k, int32_t* __restrict__ row_token,
                                  int32_t* __restrict__ inv_row) {
-  __shared__ int scan[kCapThreads];
+  constexpr int kWaves = kCapThreads / 64;
+  __shared__ int wave_kept[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   int running = 0;
+  // the next chunk's key and slot are loaded while this chunk is ranked
+  uint64_t key_n = threadIdx.x < static_cast<unsigned>(c) ? keys[threadIdx.x] : 0ull;
+  int slot_n = threadIdx.x < static_cast<unsigned>(c) ? slots[threadIdx.x] : 0;
   for (int c0 = 0; c0 < c; c0 += kCapThreads) {
     const int i = c0 + threadIdx.x;
-    const int keep = (i < c && keys[i] >= tau) ? 1 : 0;
-    scan[threadIdx.x] = keep;
-    __syncthreads();
-    for (int o = 1; o < kCapThreads; o <<= 1) {
-      const int a = threadIdx.x >= o ? scan[threadIdx.x - o] : 0;
-      __syncthreads();
-      scan[threadIdx.x] += a;
-      __syncthreads();
+    const uint64_t key = key_n;
+    const int slot = slot_n;
+    const int inext = i + kCapThreads;
+    if (inext < c) {
+      key_n = keys[inext];
+      slot_n = slots[inext];
     }
-    const int excl = scan[threadIdx.x] - keep;
-    const int chunk_total = scan[kCapThreads - 1];
+    const bool keep = i < c && key >= tau;
+    // rank inside the chunk: kept lanes of earlier waves, then of lower
+    // lanes of this wave (ballot and popcount)
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wave_kept[w] = __popcll(m);
+    __syncthreads();
+    int before = 0, chunk_total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const int x = wave_kept[v];
+      before += v < w ? x : 0;
+      chunk_total += x;
+    }
+    const int excl = before + __popcll(m & ((1ull << lane) - 1ull));
     if (i < c) {
-      const int slot = slots[i];
       if (keep) {
         const int row = base_row + running + excl;
         inv_row[slot] = row;
@@ -271,7 +342,7 @@ __device__ void assign_kept_rows(const uint64_t* __restrict__ keys,
       }
     }
     running += chunk_total;
-    __syncthreads();
+    __syncthreads();  // wave_kept is rewritten by the next chunk
   }
 }
 
