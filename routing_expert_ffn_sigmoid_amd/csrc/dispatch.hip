@@ -132,11 +132,18 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
   const int e = threadIdx.x;
   int run = 0;
   if (e < N) {
-    for (int b = 0; b < nb; ++b) {
-      const int64_t o = static_cast<int64_t>(b) * N + e;
-      const int c = block_counts[o];
-      block_base[o] = run;
-      run += c;
+    // eight blocks' counts are loaded before they are added, so their
+    // loads overlap instead of one latency per block
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int c8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c8[j] = b0 + j < nb ? block_counts[static_cast<int64_t>(b0 + j) * N + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < nb) block_base[static_cast<int64_t>(b0 + j) * N + e] = run;
+        run += c8[j];
+      }
     }
   }
   const int c_e = e < N ? run : 0;
