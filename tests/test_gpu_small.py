@@ -262,6 +262,45 @@ def test_combine_and_bias_update_match_oracle():
     np.testing.assert_array_equal(bt.cpu().numpy(), oracle.bias_update(counts, bias, 0.001))
 
 
+def test_combine_rounds_once_to_nearest_even():
+    """The combine accumulates in fp32 and rounds once to bf16, to nearest
+    with ties to even.  Inputs are chosen so that every product and sum is
+    exact in fp32 (small integer gates, values on a 2^-8 grid below 2^12),
+    so the expected output is the round-to-nearest-even of the exact sum,
+    computed here from the definition; about half the outputs are ties."""
+    require_gpu()
+    rng = np.random.default_rng(33)
+    T, H, k, M = 64, 256, 3, 200
+    wl = workloads.V3_PREFILL.with_(T=T, H=H, N=16, n_groups=1, topk_groups=1, k=k, I=64)
+    cfg = moe.make_cfg(wl)
+    # bf16 values: odd multiples of 2^-8 (|m| < 256), shared values with an
+    # exponent that puts the sum's rounding bit at 2^-8 or 2^-7
+    y_np = (rng.integers(-127, 128, size=(M, H)) * 2 + 1).astype(np.float32) / 256.0
+    ysh_np = rng.choice(np.array([1.0, -1.0, 2.0, -2.0, 1.5, 3.0], np.float32), size=(T, H))
+    inv = rng.permutation(M)[:T * k].reshape(T, k).astype(np.int32)
+    inv[rng.random((T, k)) < 0.2] = -1
+    gate = rng.integers(1, 4, size=(T, k)).astype(np.float32)
+    y = torch.from_numpy(y_np).to(torch.bfloat16).cuda()
+    ysh = torch.from_numpy(ysh_np).to(torch.bfloat16).cuda()
+    assert torch.equal(y.float().cpu(), torch.from_numpy(y_np))  # inputs exact in bf16
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(cfg, y, torch.from_numpy(inv).cuda(), torch.from_numpy(gate).cuda(), ysh, out)
+    torch.cuda.synchronize()
+    exact = ysh_np.astype(np.float64).copy()
+    for j in range(k):
+        kept = inv[:, j] >= 0
+        exact[kept] += gate[kept, j, None].astype(np.float64) * y_np[inv[kept, j]].astype(np.float64)
+    f32 = exact.astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), exact)  # the sum is exact in fp32
+    u = f32.view(np.uint32).astype(np.uint64)
+    want = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    ties = int(((u & 0xFFFF) == 0x8000).sum())
+    say(f"combine rounding: {ties} ties of {u.size}")
+    assert ties > u.size // 8
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.parametrize("T", [96, 600])
 def test_granular_calls_compose_to_layer_forward(T):
     """route -> permute -> grouped_ffn -> combine gives the layer's output, and
