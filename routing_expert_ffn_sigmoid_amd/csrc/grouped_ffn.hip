@@ -856,6 +856,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // with no LDS waits between its MFMAs.  Gate/up tiles store h straight from
 // registers, group 0 while group 1 runs the last MFMAs; down tiles (256
 // output columns) go through the staged epilogue.
+// Gate/up tiles (pp_tile_gu) keep their activation rows in two buffers of
+// 128-byte rows, each holding two k-steps, so a wave's activation load
+// covers 8 whole 128-byte lines instead of half of 16; down tiles (pp_tile)
+// keep four stages of 64-byte rows, whose fewer address registers let the
+// 9- and 10-block tiles fit the register file.
 // ---------------------------------------------------------------------
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
@@ -879,6 +884,7 @@ __device__ __forceinline__ void pp_wait_stages(bool extra) {
   }
 }
 
+// Down tile of the ping-pong kernel (the gate/up phase runs pp_tile_gu)
 template <int NMBW, bool SWIGLU>
 __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
                                      bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
@@ -1056,6 +1062,174 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   }
 }
 
+
+// wait until at most N vector-memory instructions of this wave are
+// outstanding; N < 0: no wait
+template <int N>
+__device__ __forceinline__ void pp_wait_n() {
+  if constexpr (N >= 0) wait_vmcnt<N>();
+}
+
+// Gate/up tile of the ping-pong kernel (SwiGLU epilogue).  Same phases,
+// weight stages and fragments as pp_tile; the activations of k-steps 2i and
+// 2i + 1 arrive together as 128-byte rows in buffer X0 (i even) or X1
+// (i odd).
+template <int NMBW>
+__device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                        bf16_t* X0, bf16_t* X1, bf16_t* B0, bf16_t* B1,
+                                        bf16_t* B2, bf16_t* B3) {
+  static_assert(NMBW >= 1 && NMBW <= 8, "gate/up tiles hold at most 256 rows");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int K = wave_uniform(g.K);
+  const int nk = K / kBK4;  // multiple of 4
+
+  // Activation loads: 8 rows x 128 bytes per wave instruction; row group
+  // q = p*8 + wave covers tile rows [8q, 8q+8); lane -> row 8q + lane/8,
+  // physical chunk lane%8, logical chunk (lane%8) ^ ((row >> 1) & 7), and
+  // (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.  Rows past the
+  // tile's valid ones repeat its last row; groups past the tile's height
+  // are not loaded.
+  const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
+  constexpr int G8 = 4 * NMBW;  // row groups of 8 the tile loads
+  constexpr int NAG = (G8 + 7) / 8;
+  uint32_t aoff[NAG];
+#pragma unroll
+  for (int p = 0; p < NAG; ++p) {
+    int prow = mrow0 + min((p * 8 + wave) * 8 + (lane >> 3), mv - 1);
+    if (g.row_index) prow = g.row_index[prow];
+    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+  }
+  // weights as in pp_tile: gate block `wave` and the matching up block
+  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
+  const uint32_t boff = static_cast<uint32_t>(nt * 128 + wave * 16) * krow_bytes + lane * 16u;
+  const uint32_t bsoff1 = static_cast<uint32_t>(g.up_off) * krow_bytes;
+
+  // k-steps step, step + 1 (step even)
+  auto issue_a = [&](int step, bf16_t* Xb) {
+    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
+#pragma unroll
+    for (int p = 0; p < NAG; ++p)
+      if (p * 8 + wave < G8) dma16(ra, aoff[p], kb, Xb + (p * 8 + wave) * 8 * (2 * kBK4));
+  };
+  auto issue_w = [&](int step, bf16_t* Bb) {
+    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
+    dma16(rb, boff, kw, Bb + wave * kTileElems);
+    dma16(rb, boff, bsoff1 + kw, Bb + (8 + wave) * kTileElems);
+  };
+  // activation loads of this wave per pair of k-steps: NA0, one more with
+  // `extra`
+  constexpr int NA0 = G8 / 8;
+  const bool extra = wave < (G8 % 8);
+
+  // fragments: row 16*block + lane%16 has swizzle term (lane%16) >> 1
+  const int swz = (lane & 15) >> 1;
+  const int arow = (wm * 16 + (lane & 15)) * (2 * kBK4);
+  bf16x8 af[NMBW], bf[4];
+  auto read = [&](const bf16_t* Xb, int half, const bf16_t* Bb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      bf[nb] = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<true>(wn, nb) * kTileElems));
+    const bf16_t* abase = Xb + arow + (((half * 4 + (lane >> 4)) ^ swz) * 8);
+#pragma unroll
+    for (int j = 0; j < NMBW; ++j)
+      af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * (2 * kBK4)));
+  };
+
+  f32x4 acc[NMBW][4];
+#pragma unroll
+  for (int j = 0; j < NMBW; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&]() {
+#pragma unroll
+    for (int j = 0; j < NMBW; ++j)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
+  };
+
+  // prologue: A(0,1) W0 W1 A(2,3) W2 W3; k-step 0 needs A(0,1) and W0
+  issue_a(0, X0);
+  issue_w(0, B0);
+  issue_w(1, B1);
+  issue_a(2, X1);
+  issue_w(2, B2);
+  issue_w(3, B3);
+  if (extra) wait_vmcnt<6 + NA0 + 1>();
+  else wait_vmcnt<6 + NA0>();
+  __builtin_amdgcn_s_barrier();
+  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
+  __builtin_amdgcn_sched_barrier(0);
+  // k-step k reads stage k in phase 2k (group 0) or 2k + 1 (group 1) and
+  // computes it in the phase after.  At the start of its read phase a wave
+  // issues W(k + 3) into the weight buffer of k - 1 and, for even k, first
+  // A(k + 2, k + 3) into the activation buffer of k - 2 and k - 1; both
+  // groups read k - 1 by phase 2k - 1.  Before the barrier that closes phase
+  // 2k + 1 every wave waits for its own loads of stage k + 1.  Even k:
+  // W(k + 1), then W(k + 2), A(k + 2, k + 3) and W(k + 3) may stay
+  // outstanding.  Odd k: A(k + 1, k + 2) (after W(k + 1)), then W(k + 2) and
+  // W(k + 3) may.  In the last four k-steps nothing is issued after k = nk - 4,
+  // so fewer stay outstanding.  The LDS reads of a read phase are complete
+  // (lgkmcnt 0) before its barrier.
+#define PP_WAIT(I)                                                     \
+  if (last) {                                                          \
+    if constexpr ((I) == 0) {                                          \
+      if (extra) pp_wait_n<4 + NA0 + 1>();                             \
+      else pp_wait_n<4 + NA0>();                                       \
+    } else if constexpr ((I) == 1) {                                   \
+      pp_wait_n<2>();                                                  \
+    } else if constexpr ((I) == 2) {                                   \
+      pp_wait_n<0>();                                                  \
+    }                                                                  \
+  } else if constexpr (((I) & 1) == 0) {                               \
+    if (extra) pp_wait_n<4 + NA0 + 1>();                               \
+    else pp_wait_n<4 + NA0>();                                         \
+  } else {                                                             \
+    pp_wait_n<4>();                                                    \
+  }
+#define PP_STEP(I, XR, BR, XI, BI)              \
+  {                                             \
+    const int k = st + (I);                     \
+    if (k >= 1 && k + 3 < nk) {                 \
+      if (((I) & 1) == 0) issue_a(k + 2, XI);   \
+      issue_w(k + 3, BI);                       \
+    }                                           \
+    read(XR, (I) & 1, BR);                      \
+    wait_lgkmcnt0();                            \
+    if (grp) { PP_WAIT(I) }                     \
+    __builtin_amdgcn_sched_barrier(0);          \
+    __builtin_amdgcn_s_barrier();               \
+    __builtin_amdgcn_sched_barrier(0);          \
+    compute();                                  \
+    if (!grp) { PP_WAIT(I) }                    \
+    __builtin_amdgcn_sched_barrier(0);          \
+    __builtin_amdgcn_s_barrier();               \
+    __builtin_amdgcn_sched_barrier(0);          \
+  }
+  for (int st = 0; st < nk; st += kStages) {
+    const bool last = st + kStages >= nk;  // the last four k-steps
+    PP_STEP(0, X0, B0, X1, B3)
+    PP_STEP(1, X0, B1, X1, B0)
+    PP_STEP(2, X1, B2, X0, B1)
+    PP_STEP(3, X1, B3, X0, B2)
+  }
+#undef PP_STEP
+#undef PP_WAIT
+  // group 0 stores h while group 1 runs the last MFMAs; its extra barrier
+  // pairs with group 1's last one, and no LDS is read after it
+  big_epilogue<NMBW, true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+  if (!grp) __builtin_amdgcn_s_barrier();
+}
+
 // pp_tile for the instantiated height covering nmbw M-blocks per wave
 template <int N, bool SWIGLU>
 __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, int nt, int mrow0,
@@ -1064,35 +1238,26 @@ __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, 
                                             bf16_t* B3) {
   if constexpr (N > 1) {
     if (nmbw >= N) {
-      pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+      if constexpr (SWIGLU) pp_tile_gu<N>(g, s, nt, mrow0, mv, A0, A2, B0, B1, B2, B3);
+      else pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
       return;
     }
     pp_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
   } else {
-    pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    if constexpr (SWIGLU) pp_tile_gu<1>(g, s, nt, mrow0, mv, A0, A2, B0, B1, B2, B3);
+    else pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
   }
 }
 
-// Persistent ping-pong kernel over the tiles of both groups: rounds of
+// Persistent ping-pong loop over the tiles of both groups: rounds of
 // gridDim.x tiles, inside a round XCD x takes the x-th run of gridDim.x / 8
 // tiles (tiles sharing activation rows or weights in one L2), tile_nm order
-// inside a segment.
+// inside a segment.  Gate/up tiles take A0 and A2 as their two activation
+// buffers of 128-byte rows.
 template <bool SWIGLU, int ROWS>
-__global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
-  // at most 3 activation row groups of 16 per wave and stage; at most 10
-  // M-blocks per wave fit the register file without spills
-  static_assert(ROWS % 32 == 0 && ROWS <= 320, "tile rows");
-  __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
-  __shared__ int tstart[kMaxSegs + 1];
-  __shared__ int tmp[kThreads];
-
+__device__ __forceinline__ void pp_run(const FfnLaunch& a, bf16_t* A0, bf16_t* A1, bf16_t* A2,
+                                       bf16_t* A3, bf16_t* B0, bf16_t* B1, bf16_t* B2,
+                                       bf16_t* B3, int* tstart, int* tmp) {
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
   if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
   else build_tile_starts_idle();
@@ -1122,6 +1287,32 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
     pp_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+  }
+}
+
+template <bool SWIGLU, int ROWS>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
+  // at most 3 activation row groups of 16 per wave and stage; at most 10
+  // M-blocks per wave fit the register file without spills
+  static_assert(ROWS % 32 == 0 && ROWS <= 320, "tile rows");
+  static_assert(!SWIGLU || ROWS <= 256, "gate/up tiles hold at most 256 rows");
+  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+  if constexpr (SWIGLU) {
+    // two buffers of 128-byte rows, each two k-steps
+    __shared__ __attribute__((aligned(16))) bf16_t X0[ROWS * 2 * kBK4];
+    __shared__ __attribute__((aligned(16))) bf16_t X1[ROWS * 2 * kBK4];
+    pp_run<SWIGLU, ROWS>(a, X0, X0, X1, X1, B0, B1, B2, B3, tstart, tmp);
+  } else {
+    __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
+    __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
+    __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
+    __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
+    pp_run<SWIGLU, ROWS>(a, A0, A1, A2, A3, B0, B1, B2, B3, tstart, tmp);
   }
 }
 
