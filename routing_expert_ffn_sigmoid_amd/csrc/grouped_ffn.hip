@@ -376,28 +376,6 @@ __global__ __launch_bounds__(kThreads, MOE_FFN_MINBLK) void ffn_bf16_kernel(FfnL
 constexpr int kBigRows = 256;   // max rows per tile
 constexpr int kBigBufElems = 256 * kBK;
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (scalar branches)
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<15>(); break;  // n > 15 never occurs: at most 3 stages x 5 loads
-  }
-}
-
 constexpr int kBigThreads = 512;  // 8 waves, 2 per SIMD
 
 // Wave (wm, wn) = (wave & 1, wave >> 1): M-blocks 2j + wm (j < NMBW), four
@@ -845,8 +823,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // ---------------------------------------------------------------------
 // Ping-pong kernel (large segments, K % 128 = 0: both phases of the
 // V3-shaped prefill layers, the gate/up phase of v1/v2).  Tiles of up to
-// kTileRows* activation rows x 256 weight rows, k-steps of 32, four LDS
-// stages of both operands filled by direct global->LDS loads.
+// 256 activation rows x 256 weight rows, k-steps of 32, four weight stages
+// and two activation buffers filled by direct global->LDS loads.
 // The dispatcher places waves w and w + 4 of a workgroup on the same SIMD.
 // Group 0 (waves 0-3) and group 1 (waves 4-7) run half a k-step apart: in
 // every phase (closed by a workgroup barrier) one group reads a whole
@@ -856,212 +834,20 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // with no LDS waits between its MFMAs.  Gate/up tiles store h straight from
 // registers, group 0 while group 1 runs the last MFMAs; down tiles (256
 // output columns) go through the staged epilogue.
-// Gate/up tiles (pp_tile_gu) keep their activation rows in two buffers of
-// 128-byte rows, each holding two k-steps, so a wave's activation load
-// covers 8 whole 128-byte lines instead of half of 16; down tiles (pp_tile)
-// keep four stages of 64-byte rows, whose fewer address registers let the
-// 9- and 10-block tiles fit the register file.
+// An activation buffer holds two k-steps as 128-byte rows, so one wave's
+// activation load covers 8 whole 128-byte lines.  (Loading each k-step as
+// 64-byte rows, half of 16 lines per load, measured 6 % slower on both
+// phases of the V3-shaped prefill layer.)
 // ---------------------------------------------------------------------
 constexpr int kBK4 = 32;
 constexpr int kStages = 4;
 constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
-// Activation rows per tile (a multiple of 32, at most 384), per phase.
-// Taller tiles keep an expert slightly over 256 rows in one tile and load
-// its weights once; measured on the V3-shaped layers, 320 rows are 4 %
-// faster than 256 on the down phase (K = 2048) but 5 % slower on gate/up
-// (K = 7168, 288 rows: 1 % slower; the 9- and 10-block tiles' longer
-// phases cost more than the saved weight loads).
-constexpr int kTileRowsGateUp = 256;
-constexpr int kTileRowsDown = 320;
-
-// s_waitcnt allowing N stages of a wave's loads to stay outstanding, a stage
-// being OPS0 loads, or OPS0 + 1 on waves with `extra` set; N < 0: no wait
-template <int OPS0, int N>
-__device__ __forceinline__ void pp_wait_stages(bool extra) {
-  if constexpr (N >= 0) {
-    if (extra) wait_vmcnt<N * (OPS0 + 1)>();
-    else wait_vmcnt<N * OPS0>();
-  }
-}
-
-// Down tile of the ping-pong kernel (the gate/up phase runs pp_tile_gu)
-template <int NMBW, bool SWIGLU>
-__device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                     bf16_t* A0, bf16_t* A1, bf16_t* A2, bf16_t* A3,
-                                     bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int grp = wave >> 2;  // 0: reads first; 1: half a k-step later
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int K = wave_uniform(g.K);
-  const int nk = K / kBK4;  // multiple of 4
-
-  // Activation loads: 16 rows x 64 bytes per wave instruction; row group
-  // q = p*8 + wave covers tile rows [16q, 16q+16); lane -> row 16q + lane/4,
-  // physical chunk lane%4, logical chunk (lane%4) ^ ((row >> 1) & 3), and
-  // (row >> 1) & 3 = (lane >> 3) & 3 for every q.  (With 64-byte rows this
-  // XOR of row pairs keeps the 16-byte fragment reads free of bank
-  // conflicts on gfx950; XOR by row quads does not.)  Rows past the tile's
-  // valid ones repeat its last row; groups past the tile's height are not
-  // loaded.
-  const int logical = (lane & 3) ^ ((lane >> 3) & 3);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
-  const int rows_needed = (2 * NMBW) * 16;
-  constexpr int NAG = (2 * NMBW + 7) / 8;
-  uint32_t aoff[NAG];
-  bool aact[NAG];
-#pragma unroll
-  for (int p = 0; p < NAG; ++p) {
-    const int row = (p * 8 + wave) * 16 + (lane >> 2);
-    int prow = mrow0 + min(row, mv - 1);
-    if (g.row_index) prow = g.row_index[prow];
-    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
-    aact[p] = (p * 8 + wave) * 16 < rows_needed;  // wave-uniform
-  }
-  // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
-  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
-  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.
-  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const uint32_t boff =
-      static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
-  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
-
-  // cnt counts this wave's vector-memory instructions; mark[b] is cnt right
-  // after the loads of the stage in buffer b, so waiting for that stage is
-  // vmcnt(cnt - mark[b])
-  int cnt = 0;
-  int mark[kStages] = {0, 0, 0, 0};
-  auto issue = [&](int step, bf16_t* Ab, bf16_t* Bb) {
-    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
-#pragma unroll
-    for (int p = 0; p < NAG; ++p)
-      if (aact[p]) {
-        dma16(ra, aoff[p], kb, Ab + (p * 8 + wave) * 16 * kBK4);
-        ++cnt;
-      }
-    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
-    dma16(rb, boff, kw, Bb + wave * kTileElems);
-    dma16(rb, boff, bsoff1 + kw, Bb + (8 + wave) * kTileElems);
-    cnt += 2;
-  };
-  auto wait_stage = [&](int b) { wait_vmcnt_dyn(cnt - mark[b]); };
-  // Per stage every wave issues 2 weight loads and G / 8 activation groups,
-  // one more on the first G % 8 waves (G = 2 * NMBW groups of 16 rows dealt
-  // round-robin), so "at most n stages outstanding" is a constant vmcnt
-  // picked by one wave-uniform branch.  The run-time wait above (a tree of
-  // scalar branches) cost 11 % of a compute-only down launch; tiles of 9 or
-  // 10 M-blocks keep it, since with constant waits the compiler spills
-  // their registers.
-  constexpr int G = 2 * NMBW;
-  const bool extra = wave < (G % 8);
-
-  // a whole k-step's fragments: M-blocks 2j + wm (j < NMBW), weight blocks
-  // of columns 32wn .. 32wn + 31 (gate and up)
-  const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
-  const int aoffs = (wm * 16 + (lane & 15)) * kBK4 + ch * 8;
-  bf16x8 af[NMBW], bf[4];
-  auto read = [&](const bf16_t* Ab, const bf16_t* Bb) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bf[nb] = as_bf16x8(
-          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<SWIGLU>(wn, nb) * kTileElems));
-#pragma unroll
-    for (int j = 0; j < NMBW; ++j)
-      af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ab + aoffs + j * 32 * kBK4));
-  };
-
-  f32x4 acc[NMBW][4];
-#pragma unroll
-  for (int j = 0; j < NMBW; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&]() {
-#pragma unroll
-    for (int j = 0; j < NMBW; ++j)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
-  };
-
-  issue(0, A0, B0);
-  mark[0] = cnt;
-  issue(1, A1, B1);
-  mark[1] = cnt;
-  issue(2, A2, B2);
-  mark[2] = cnt;
-  issue(3, A3, B3);
-  mark[3] = cnt;
-  wait_stage(0);
-  __builtin_amdgcn_s_barrier();
-  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
-  __builtin_amdgcn_sched_barrier(0);
-  // k-step k reads stage k (buffer k % 4): group 0 in phase 2k, group 1 in
-  // phase 2k + 1; each computes it in the phase after.  At the start of its
-  // read phase a wave issues its part of stage k + 3 (k >= 1) into buffer
-  // (k + 3) % 4, which last held k-step k - 1, read by both groups by phase
-  // 2k - 1.  Before the barrier that closes phase 2k + 1 every wave waits
-  // for its own loads of stage k + 1, which group 0 reads in phase 2k + 2;
-  // after them stages k + 2 and k + 3 may be outstanding, in the last four
-  // k-steps fewer.  The LDS reads of a read phase are complete (lgkmcnt 0)
-  // before its barrier.
-#define PP_WAIT(I)                                                   \
-  if constexpr (NMBW > 8) {                                          \
-    wait_stage(((I) + 1) % 4);                                       \
-  } else {                                                           \
-    if (last) pp_wait_stages<2 + G / 8, 2 - (I)>(extra);             \
-    else pp_wait_stages<2 + G / 8, 2>(extra);                        \
-  }
-#define PP_STEP(I, AR, BR, AI, BI)              \
-  {                                             \
-    const int k = st + (I);                     \
-    if (k >= 1 && k + 3 < nk) {                 \
-      issue(k + 3, AI, BI);                     \
-      mark[((I) + 3) % 4] = cnt;                \
-    }                                           \
-    read(AR, BR);                               \
-    wait_lgkmcnt0();                            \
-    if (grp) { PP_WAIT(I) }                     \
-    __builtin_amdgcn_sched_barrier(0);          \
-    __builtin_amdgcn_s_barrier();               \
-    __builtin_amdgcn_sched_barrier(0);          \
-    compute();                                  \
-    if (!grp) { PP_WAIT(I) }                    \
-    __builtin_amdgcn_sched_barrier(0);          \
-    __builtin_amdgcn_s_barrier();               \
-    __builtin_amdgcn_sched_barrier(0);          \
-  }
-  for (int st = 0; st < nk; st += kStages) {
-    const bool last = st + kStages >= nk;  // the last four k-steps
-    PP_STEP(0, A0, B0, A3, B3)
-    PP_STEP(1, A1, B1, A0, B0)
-    PP_STEP(2, A2, B2, A1, B1)
-    PP_STEP(3, A3, B3, A2, B2)
-  }
-#undef PP_STEP
-#undef PP_WAIT
-  // Group 0's extra barrier pairs with group 1's last one, so both groups
-  // pass the same number of barriers per tile.
-  if (SWIGLU) {
-    // group 0 stores h while group 1 runs the last MFMAs; no LDS is read
-    // after the extra barrier, so the next tile's loads need no other one
-    big_epilogue<sizeof(acc) / sizeof(acc[0]), true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
-    if (!grp) __builtin_amdgcn_s_barrier();
-  } else {
-    // staging in B1/B2: every read phase ended with lgkmcnt(0) before its
-    // barrier (group 1's last one closes phase 2nk - 1) and every load was
-    // waited for, so both buffers are free
-    if (!grp) __builtin_amdgcn_s_barrier();
-    staged_epilogue<sizeof(acc) / sizeof(acc[0]), false>(g, acc, NMBW, wm, wn, nt, mrow0, mv,
-                                                         B1, B2);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();  // staging reads done before the next tile's loads
-  }
-}
-
+// Activation rows per tile.  Taller tiles would keep an expert slightly over
+// 256 rows in one tile and load its weights once, but 9 or 10 M-blocks per
+// wave spill registers with this layout's address registers; with 64-byte
+// rows, 320-row down tiles had been 4 % faster than 256 and 320-row gate/up
+// tiles 5 % slower.
+constexpr int kPPRows = 256;
 
 // wait until at most N vector-memory instructions of this wave are
 // outstanding; N < 0: no wait
@@ -1070,15 +856,14 @@ __device__ __forceinline__ void pp_wait_n() {
   if constexpr (N >= 0) wait_vmcnt<N>();
 }
 
-// Gate/up tile of the ping-pong kernel (SwiGLU epilogue).  Same phases,
-// weight stages and fragments as pp_tile; the activations of k-steps 2i and
+// One tile of the ping-pong kernel; the activations of k-steps 2i and
 // 2i + 1 arrive together as 128-byte rows in buffer X0 (i even) or X1
 // (i odd).
-template <int NMBW>
-__device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                        bf16_t* X0, bf16_t* X1, bf16_t* B0, bf16_t* B1,
-                                        bf16_t* B2, bf16_t* B3) {
-  static_assert(NMBW >= 1 && NMBW <= 8, "gate/up tiles hold at most 256 rows");
+template <int NMBW, bool SWIGLU>
+__device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
+                                     bf16_t* X0, bf16_t* X1, bf16_t* B0, bf16_t* B1, bf16_t* B2,
+                                     bf16_t* B3) {
+  static_assert(NMBW >= 1 && NMBW <= 8, "tiles hold at most 256 rows");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
@@ -1107,10 +892,13 @@ __device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mr
     if (g.row_index) prow = g.row_index[prow];
     aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
   }
-  // weights as in pp_tile: gate block `wave` and the matching up block
+  // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
+  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
+  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const uint32_t boff = static_cast<uint32_t>(nt * 128 + wave * 16) * krow_bytes + lane * 16u;
-  const uint32_t bsoff1 = static_cast<uint32_t>(g.up_off) * krow_bytes;
+  const uint32_t boff =
+      static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
+  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
 
   // k-steps step, step + 1 (step even)
   auto issue_a = [&](int step, bf16_t* Xb) {
@@ -1129,7 +917,9 @@ __device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mr
   constexpr int NA0 = G8 / 8;
   const bool extra = wave < (G8 % 8);
 
-  // fragments: row 16*block + lane%16 has swizzle term (lane%16) >> 1
+  // a whole k-step's fragments: M-blocks 2j + wm (j < NMBW), weight blocks
+  // of columns 32wn .. 32wn + 31 (gate and up); row 16*block + lane%16 has
+  // swizzle term (lane%16) >> 1
   const int swz = (lane & 15) >> 1;
   const int arow = (wm * 16 + (lane & 15)) * (2 * kBK4);
   bf16x8 af[NMBW], bf[4];
@@ -1137,7 +927,7 @@ __device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mr
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       bf[nb] = as_bf16x8(
-          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<true>(wn, nb) * kTileElems));
+          *reinterpret_cast<const u32x4*>(Bb + lane * 8 + big_wblock<SWIGLU>(wn, nb) * kTileElems));
     const bf16_t* abase = Xb + arow + (((half * 4 + (lane >> 4)) ^ swz) * 8);
 #pragma unroll
     for (int j = 0; j < NMBW; ++j)
@@ -1224,40 +1014,56 @@ __device__ __noinline__ void pp_tile_gu(const FfnGroup& g, int s, int nt, int mr
   }
 #undef PP_STEP
 #undef PP_WAIT
-  // group 0 stores h while group 1 runs the last MFMAs; its extra barrier
-  // pairs with group 1's last one, and no LDS is read after it
-  big_epilogue<NMBW, true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
-  if (!grp) __builtin_amdgcn_s_barrier();
+  // Group 0's extra barrier pairs with group 1's last one, so both groups
+  // pass the same number of barriers per tile.
+  if constexpr (SWIGLU) {
+    // group 0 stores h while group 1 runs the last MFMAs; no LDS is read
+    // after the extra barrier, so the next tile's loads need no other one
+    big_epilogue<NMBW, true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+    if (!grp) __builtin_amdgcn_s_barrier();
+  } else {
+    // staging in B1/B2: every read phase ended with lgkmcnt(0) before its
+    // barrier (group 1's last one closes phase 2nk - 1) and every load was
+    // waited for, so both buffers are free
+    if (!grp) __builtin_amdgcn_s_barrier();
+    staged_epilogue<NMBW, false>(g, acc, NMBW, wm, wn, nt, mrow0, mv, B1, B2);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();  // staging reads done before the next tile's loads
+  }
 }
 
 // pp_tile for the instantiated height covering nmbw M-blocks per wave
 template <int N, bool SWIGLU>
 __device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, int nt, int mrow0,
-                                            int mv, bf16_t* A0, bf16_t* A1, bf16_t* A2,
-                                            bf16_t* A3, bf16_t* B0, bf16_t* B1, bf16_t* B2,
-                                            bf16_t* B3) {
+                                            int mv, bf16_t* X0, bf16_t* X1, bf16_t* B0,
+                                            bf16_t* B1, bf16_t* B2, bf16_t* B3) {
   if constexpr (N > 1) {
     if (nmbw >= N) {
-      if constexpr (SWIGLU) pp_tile_gu<N>(g, s, nt, mrow0, mv, A0, A2, B0, B1, B2, B3);
-      else pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+      pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
       return;
     }
-    pp_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    pp_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
   } else {
-    if constexpr (SWIGLU) pp_tile_gu<1>(g, s, nt, mrow0, mv, A0, A2, B0, B1, B2, B3);
-    else pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
+    pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
   }
 }
 
-// Persistent ping-pong loop over the tiles of both groups: rounds of
+// Persistent ping-pong kernel over the tiles of both groups: rounds of
 // gridDim.x tiles, inside a round XCD x takes the x-th run of gridDim.x / 8
 // tiles (tiles sharing activation rows or weights in one L2), tile_nm order
-// inside a segment.  Gate/up tiles take A0 and A2 as their two activation
-// buffers of 128-byte rows.
-template <bool SWIGLU, int ROWS>
-__device__ __forceinline__ void pp_run(const FfnLaunch& a, bf16_t* A0, bf16_t* A1, bf16_t* A2,
-                                       bf16_t* A3, bf16_t* B0, bf16_t* B1, bf16_t* B2,
-                                       bf16_t* B3, int* tstart, int* tmp) {
+// inside a segment.
+template <bool SWIGLU>
+__global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
+  constexpr int ROWS = kPPRows;
+  __shared__ __attribute__((aligned(16))) bf16_t X0[ROWS * 2 * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t X1[ROWS * 2 * kBK4];
+  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
+  __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int tmp[kThreads];
+
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
   if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
   else build_tile_starts_idle();
@@ -1286,33 +1092,7 @@ __device__ __forceinline__ void pp_run(const FfnLaunch& a, bf16_t* A0, bf16_t* A
     const int mrow0 = r0 + mt * rpt;
     const int mv = min(rpt, rows - mt * rpt);
     const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
-    pp_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, A0, A1, A2, A3, B0, B1, B2, B3);
-  }
-}
-
-template <bool SWIGLU, int ROWS>
-__global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
-  // at most 3 activation row groups of 16 per wave and stage; at most 10
-  // M-blocks per wave fit the register file without spills
-  static_assert(ROWS % 32 == 0 && ROWS <= 320, "tile rows");
-  static_assert(!SWIGLU || ROWS <= 256, "gate/up tiles hold at most 256 rows");
-  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
-  __shared__ int tstart[kMaxSegs + 1];
-  __shared__ int tmp[kThreads];
-  if constexpr (SWIGLU) {
-    // two buffers of 128-byte rows, each two k-steps
-    __shared__ __attribute__((aligned(16))) bf16_t X0[ROWS * 2 * kBK4];
-    __shared__ __attribute__((aligned(16))) bf16_t X1[ROWS * 2 * kBK4];
-    pp_run<SWIGLU, ROWS>(a, X0, X0, X1, X1, B0, B1, B2, B3, tstart, tmp);
-  } else {
-    __shared__ __attribute__((aligned(16))) bf16_t A0[ROWS * kBK4];
-    __shared__ __attribute__((aligned(16))) bf16_t A1[ROWS * kBK4];
-    __shared__ __attribute__((aligned(16))) bf16_t A2[ROWS * kBK4];
-    __shared__ __attribute__((aligned(16))) bf16_t A3[ROWS * kBK4];
-    pp_run<SWIGLU, ROWS>(a, A0, A1, A2, A3, B0, B1, B2, B3, tstart, tmp);
+    pp_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
   }
 }
 
@@ -1367,18 +1147,19 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   bool klong = true;
   for (int i = 0; i < fl.ngroups; ++i) {
     k128 = k128 && fl.g[i].K % 128 == 0;
-    klong = klong && fl.g[i].K >= 2048;
+    klong = klong && fl.g[i].K >= 1024;
   }
 #ifndef MOE_FFN_NO_PP
   // Measured (V3 prefill: gate/up K = 7168, down K = 2048; v1 and v2:
-  // gate/up K = 2048, down K = 1408): a down phase with K < 2048 (44
-  // k-steps per tile at 1408) runs faster on the persistent 2-stage kernel,
-  // which overlaps a tile's first loads with the previous tile.
+  // gate/up K = 2048, down K = 1408): every one of these phases runs faster
+  // on the ping-pong kernel (v1 down 0.264 -> 0.238 ms, v2 down 0.331 ->
+  // 0.306 ms).  A down phase with short K keeps the persistent 2-stage
+  // kernel, which overlaps a tile's first loads with the previous tile.
   if (k128 && (phase == 0 || klong)) {
     if (phase == 0)
-      ffn_pp_kernel<true, kTileRowsGateUp><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+      ffn_pp_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     else
-      ffn_pp_kernel<false, kTileRowsDown><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
+      ffn_pp_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
 #endif

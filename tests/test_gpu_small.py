@@ -177,14 +177,15 @@ def test_bf16_small_layer_parity_and_determinism():
                                                    (400, 192, 256), (150, 2048, 256),
                                                    (400, 2048, 256), (150, 2048, 448),
                                                    (150, 128, 128), (150, 256, 4096),
-                                                   (300, 128, 4096)])
+                                                   (300, 128, 4096), (150, 1408, 256),
+                                                   (600, 1024, 384)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height.
     Large segments run the gate/up projection (K = H, a multiple of 128,
     from 128 = four k-steps, all in the kernel's last loop iteration, up to
-    4096 here) on the ping-pong kernel; an expert width of 2048 sends the
-    down projection there too (K >= 2048; with H = 448 its second column
-    tile is partial), 128-256 through the 2-stage kernel."""
+    4096 here) on the ping-pong kernel; expert widths of 1024, 1408 and 2048
+    send the down projection there too (K >= 1024; with H = 384 or 448 its
+    second column tile is partial), 128-256 through the 2-stage kernel."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
     nseg = 9
