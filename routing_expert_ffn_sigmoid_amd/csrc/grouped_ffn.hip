@@ -877,20 +877,28 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   // q = p*8 + wave covers tile rows [8q, 8q+8); lane -> row 8q + lane/8,
   // physical chunk lane%8, logical chunk (lane%8) ^ ((row >> 1) & 7), and
   // (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.  Rows past the
-  // tile's valid ones repeat its last row; groups past the tile's height
-  // are not loaded.
+  // tile's valid ones read from past the buffer's end, which returns zeros
+  // without a memory request (their results are never stored; a buffer
+  // within 256 MiB of 4 GiB repeats the last valid row instead, so that no
+  // offset wraps); groups past the tile's height are not loaded.
   const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(
       static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
   constexpr int G8 = 4 * NMBW;  // row groups of 8 the tile loads
   constexpr int NAG = (G8 + 7) / 8;
+  const bool zero_pad = g.a_bytes <= 0xF0000000u;
   uint32_t aoff[NAG];
 #pragma unroll
   for (int p = 0; p < NAG; ++p) {
-    int prow = mrow0 + min((p * 8 + wave) * 8 + (lane >> 3), mv - 1);
-    if (g.row_index) prow = g.row_index[prow];
-    aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+    const int row = (p * 8 + wave) * 8 + (lane >> 3);
+    if (row < mv || !zero_pad) {
+      int prow = mrow0 + min(row, mv - 1);
+      if (g.row_index) prow = g.row_index[prow];
+      aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
+    } else {
+      aoff[p] = g.a_bytes;
+    }
   }
   // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
   // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
