@@ -11,7 +11,11 @@
 // contiguous KiB that already holds each lane's MFMA fragment, which streams
 // from HBM measurably faster than 16 rows x 64 bytes of a row-major matrix.
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+// bf16 path (gfx950 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// Segments of 128 rows and more run the 8-wave large-tile kernels
+// (ffn_pp_kernel, ffn_big_kernel: both operands loaded straight into LDS,
+// described where they are defined); smaller segments (decode) run
+// ffn_bf16_kernel:
 //  * workgroup = 4 waves; a wave computes all BM rows of the tile times 64
 //    weight rows (4 blocks of 16).  In the gate/up phase a wave's blocks are
 //    gate columns c..c+31 and the up columns c..c+31, so the SwiGLU product
