@@ -218,6 +218,46 @@ def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
 
 
+def test_grouped_ffn_activation_buffer_within_256mib_of_4gib():
+    """An activation buffer of 4.1e9 bytes: the large-tile kernels address
+    it with 32-bit offsets, so rows past a partial tile's end repeat its last
+    valid row there instead of reading from past the buffer's end (the zero
+    padding used below that size could wrap).  Rows of every segment's
+    partial last tile and of its first tile are compared with the oracle."""
+    require_gpu()
+    H, inter = 2048, 128
+    sizes = np.array([400000, 300007, 300013])
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(offs[-1])
+    assert 0xF0000000 < M * H * 2 < 0xFFFFFFFF
+    wl = workloads.V3_PREFILL.with_(H=H, N=16, n_groups=1, topk_groups=1, k=2, I=64)
+    cfg = moe.make_cfg(wl)
+    say(f"grouped ffn near 4 GiB: M={M} H={H} inter={inter}")
+    a = synth.normal((M, H), 1.0, torch.bfloat16, "cuda", 2, "a", chunk_dim0=False)
+    w13 = synth.normal((3, 2 * inter, H), 0.02, torch.bfloat16, "cuda", 2, "w13")
+    w2 = synth.normal((3, H, inter), 0.02, torch.bfloat16, "cuda", 2, "w2")
+    y = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_grouped_ffn_workspace_size(cfg, M, inter), dtype=torch.uint8,
+                     device="cuda")
+    moe.moe_grouped_ffn(cfg, 3, torch.from_numpy(offs).cuda(), M, inter, a, None,
+                        moe.pack_weights(w13), moe.pack_weights(w2), y, ws)
+    torch.cuda.synchronize()
+    rows = []
+    for sg in range(3):
+        rows += list(range(offs[sg], offs[sg] + 3)) + list(range(offs[sg + 1] - 40, offs[sg + 1]))
+    idx = torch.tensor(rows, device="cuda")
+    an = typed(a[idx].cpu())
+    w13n, w2n = typed(w13), typed(w2)
+    ref = np.empty((len(rows), H))
+    for i, r_ in enumerate(rows):
+        sg = int(np.searchsorted(offs, r_, side="right") - 1)
+        ref[i] = oracle.swiglu_row(an[i], w13n[sg], w2n[sg])
+    got = y[idx].float().cpu().numpy().astype(np.float64)
+    mr, l2 = normwise(got, ref)
+    say(f"  max-rel {mr:.2e} rel-L2 {l2:.2e}")
+    assert mr <= BF16_MAXREL and l2 <= BF16_RELL2
+
+
 @pytest.mark.parametrize("T,I", [(1024, 192), (1500, 128)])
 def test_bf16_layer_with_large_segments(T, I):
     """Segments of ~hundreds of rows (the large-segment kernel), an odd
