@@ -444,10 +444,21 @@ __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
   }
 }
 
-template <int NJ, bool SWIGLU>
-__device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
-                                             int nmbw, int wm, int wn, int nt, int mrow0,
-                                             int mv) {
+// SwiGLU of a gate/up accumulator pair, rounded to bf16 and packed: two h
+// columns per 32-bit word (lower column in the low half)
+__device__ __forceinline__ uint32_t swiglu_pack(float g0, float g1, float u0, float u1) {
+  const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
+  const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+  return pack_bf16x2(h0, h1);
+}
+
+// Gate/up tile epilogue straight from registers: per M-block and lane, h of
+// 4 consecutive columns of one row (8 bytes) for each of the wave's two
+// 16-column blocks; rows past mv and columns past n_out are not stored.
+template <int NJ>
+__device__ __forceinline__ void gate_up_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
+                                                 int nmbw, int wm, int wn, int nt, int mrow0,
+                                                 int mv) {
   const int lane = threadIdx.x & 63;
   bf16_t* Out = static_cast<bf16_t*>(g.Out);
   const int rl = lane & 15;
@@ -458,67 +469,38 @@ __device__ __forceinline__ void big_epilogue(const FfnGroup& g, const f32x4 (&ac
       const int r = (2 * j + wm) * 16 + rl;
       if (r < mv) {
         bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
-        if (SWIGLU) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int col = nt * 128 + wn * 32 + nb * 16 + cq;
-            if (col < g.n_out) {
-              uint32_t w[2];
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const float g0 = acc[j][nb][2 * h], g1 = acc[j][nb][2 * h + 1];
-                const float u0 = acc[j][nb + 2][2 * h], u1 = acc[j][nb + 2][2 * h + 1];
-                const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
-                const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-                w[h] = pack_bf16x2(h0, h1);
-              }
-              *reinterpret_cast<u32x2*>(orow + col) = u32x2{w[0], w[1]};
-            }
-          }
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int col = nt * 256 + wn * 64 + nb * 16 + cq;
-            if (col < g.n_out) {
-              const uint32_t w0 = pack_bf16x2(acc[j][nb][0], acc[j][nb][1]);
-              const uint32_t w1 = pack_bf16x2(acc[j][nb][2], acc[j][nb][3]);
-              *reinterpret_cast<u32x2*>(orow + col) = u32x2{w0, w1};
-            }
-          }
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = nt * 128 + wn * 32 + nb * 16 + cq;
+          if (col < g.n_out)
+            *reinterpret_cast<u32x2*>(orow + col) =
+                u32x2{swiglu_pack(acc[j][nb][0], acc[j][nb][1], acc[j][nb + 2][0], acc[j][nb + 2][1]),
+                      swiglu_pack(acc[j][nb][2], acc[j][nb][3], acc[j][nb + 2][2], acc[j][nb + 2][3])};
         }
       }
     }
   }
 }
 
-// SwiGLU of a gate/up accumulator pair, rounded to bf16 and packed: two h
-// columns per 32-bit word (lower column in the low half)
-__device__ __forceinline__ uint32_t swiglu_pack(float g0, float g1, float u0, float u1) {
-  const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
-  const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
-  return pack_bf16x2(h0, h1);
-}
-
-// Tile epilogue through LDS, so the outputs leave as whole rows.  Pass p
-// covers M-block p of both wave rows (tile rows 32p .. 32p + 31): every wave
-// writes its accumulators for those rows, rounded to bf16 (SwiGLU applied in
-// the gate/up phase), into a staging buffer; after a barrier each wave reads
-// whole 1 KiB pieces of the buffer and stores them, so a store instruction
-// writes complete 128-byte lines (two 512-byte rows of a 256-column tile or
-// four 256-byte rows of a 128-column h tile) instead of 32-byte pieces of 16
-// rows, a quarter of the write requests.  The 16-byte chunk c of staged row
-// r sits at position c ^ (r % chunks per row), so the 8-byte writes of 16
-// rows and the row reads touch distinct LDS banks.  The two staging buffers
-// (16 KiB each, free when this is called) alternate, so one barrier per
-// pass orders the writes before the reads, and the reads of pass p before
-// the writes of pass p + 2 (each wave's reads complete before its stores
-// issue, which precede its arrival at the next barrier).  Rows past mv and
-// columns past n_out are not stored (n_out is a multiple of 8).
-template <int NJ, bool SWIGLU>
+// Down tile epilogue through LDS, so the outputs leave as whole rows.  Pass
+// p covers M-block p of both wave rows (tile rows 32p .. 32p + 31): every
+// wave writes its accumulators for those rows, rounded to bf16, into a
+// staging buffer; after a barrier each wave reads whole 1 KiB pieces of the
+// buffer and stores them, so a store instruction writes two whole 512-byte
+// rows (8 complete 128-byte lines) instead of 32-byte pieces of 16 rows, a
+// quarter of the write requests.  The 16-byte chunk c of staged row r sits
+// at position c ^ (r % 32), so the 8-byte writes of 16 rows and the row
+// reads touch distinct LDS banks.  The two staging buffers (16 KiB each,
+// free when this is called) alternate, so one barrier per pass orders the
+// writes before the reads, and the reads of pass p before the writes of
+// pass p + 2 (each wave's reads complete before its stores issue, which
+// precede its arrival at the next barrier).  Rows past mv and columns past
+// n_out are not stored (n_out is a multiple of 8).
+template <int NJ>
 __device__ __forceinline__ void staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
                                                 int nmbw, int wm, int wn, int nt, int mrow0,
                                                 int mv, bf16_t* S0, bf16_t* S1) {
-  constexpr int COLS = SWIGLU ? 128 : 256;  // output columns of a tile
+  constexpr int COLS = 256;                 // output columns of a tile
   constexpr int RB = COLS * 2;              // bytes of a staged row
   constexpr int CPR = RB / 16;              // 16-byte chunks per staged row
   constexpr int NI = 32 * RB / 1024;        // 1 KiB pieces per pass
@@ -532,26 +514,13 @@ __device__ __forceinline__ void staged_epilogue(const FfnGroup& g, const f32x4 (
     if (p < nmbw) {  // tile-uniform
       char* S = reinterpret_cast<char*>(p & 1 ? S1 : S0);
       char* srow = S + rloc * RB;
-      if (SWIGLU) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = wn * 32 + nb * 16 + q * 4;
-          const uint32_t w0 = swiglu_pack(acc[p][nb][0], acc[p][nb][1], acc[p][nb + 2][0],
-                                          acc[p][nb + 2][1]);
-          const uint32_t w1 = swiglu_pack(acc[p][nb][2], acc[p][nb][3], acc[p][nb + 2][2],
-                                          acc[p][nb + 2][3]);
-          *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
-              u32x2{w0, w1};
-        }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = wn * 64 + nb * 16 + q * 4;
-          const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
-          const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
-          *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
-              u32x2{w0, w1};
-        }
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = wn * 64 + nb * 16 + q * 4;
+        const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
+        const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
+        *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
+            u32x2{w0, w1};
       }
       wait_lgkmcnt0();
       __builtin_amdgcn_s_barrier();
@@ -1031,14 +1000,14 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   if constexpr (SWIGLU) {
     // group 0 stores h while group 1 runs the last MFMAs; no LDS is read
     // after the extra barrier, so the next tile's loads need no other one
-    big_epilogue<NMBW, true>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
+    gate_up_epilogue<NMBW>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
     if (!grp) __builtin_amdgcn_s_barrier();
   } else {
     // staging in B1/B2: every read phase ended with lgkmcnt(0) before its
     // barrier (group 1's last one closes phase 2nk - 1) and every load was
     // waited for, so both buffers are free
     if (!grp) __builtin_amdgcn_s_barrier();
-    staged_epilogue<NMBW, false>(g, acc, NMBW, wm, wn, nt, mrow0, mv, B1, B2);
+    staged_epilogue<NMBW>(g, acc, NMBW, wm, wn, nt, mrow0, mv, B1, B2);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();  // staging reads done before the next tile's loads
   }
