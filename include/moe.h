@@ -76,7 +76,13 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
 
 /* Score function.  SIGMOID: s = 1/(1+e^-l), each expert independent
  * ([EVO] §DeepSeek-v3).  SOFTMAX: s = softmax over the N logits ([EVO]
- * §ST-MoE p_i(x); §DeepSeek-v1/v2 gate). */
+ * §ST-MoE p_i(x); §DeepSeek-v1/v2 gate).  Both are computed in fp32 with
+ * every rounding step fixed, so a score is reproducible bit for bit: the
+ * exponential is Cody-Waite reduction plus a degree-7 Taylor series; the
+ * softmax takes E_e = e^(l_e - m) with m the largest logit (E_e = 0 when
+ * l_e - m < -64), S = the pairwise sum of E over 256 slots (slot e >= N
+ * holds 0; each node adds its lower half's sum to its upper half's), and
+ * s_e = E_e / S correctly rounded. */
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
 typedef struct {
@@ -320,9 +326,16 @@ moe_status moe_group_load_stats(const moe_cfg* cfg, const float* f, const float*
 moe_status moe_bias_update(const moe_cfg* cfg, const int32_t* counts,
                            float* bias, float u, void* stream);
 
-/* The whole layer: out [T,H] = shared(x) + sum of gated routed experts.
+/* The whole layer ([BUILD] §2.2, the layer's forward pass: the shared
+ * experts' output plus the gate-weighted outputs of the routed experts the
+ * router picked; [EVO] §DeepSeek-v3 and [GLR] §1, §3 for the routing):
+ *   out [T,H] = shared(x) + sum of gated routed experts, the calls above
+ * run in order (router GEMM, route, dispatch, grouped SwiGLU for the routed
+ * and shared experts, combine, load statistics) on one stream.
  * x [T,H] act_dtype; bias [N] f32 or NULL; aux NULL or as above.
- * Workspace: moe_workspace_size(cfg). */
+ * Workspace: moe_workspace_size(cfg); MOE_ERR_WORKSPACE if ws is NULL or
+ * smaller.  Errors as for the granular calls, all detected before any
+ * launch. */
 moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* weights,
                              const void* x, const float* bias, void* out,
                              const moe_aux* aux, void* ws, size_t ws_bytes,

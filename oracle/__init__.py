@@ -49,6 +49,8 @@ def lib():
         L.orc_sigmoid32.restype = ctypes.c_float
         L.orc_sigmoid32.argtypes = [ctypes.c_float]
         L.orc_sigmoid32_array.argtypes = [_vp, _vp, _i64]
+        L.orc_softmax32.restype = _i
+        L.orc_softmax32.argtypes = [_i, _vp, _vp]
         L.orc_router_logits.argtypes = [_i, _i, _i, _vp, _i, _vp, _i, _vp]
         L.orc_route.restype = _i
         L.orc_route.argtypes = [ctypes.POINTER(RouteCfg), _vp, _vp, _vp, _vp,
@@ -92,6 +94,19 @@ def sigmoid32(l: np.ndarray) -> np.ndarray:
     l = np.ascontiguousarray(l, dtype=np.float32)
     out = np.empty_like(l)
     lib().orc_sigmoid32_array(_ptr(l), _ptr(out), l.size)
+    return out
+
+
+def softmax32(logits: np.ndarray) -> np.ndarray:
+    """The fp32 softmax score of each row of logits [T, N] (N <= 256)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    if logits.ndim == 1:
+        logits = logits[None, :]
+    T, N = logits.shape
+    out = np.empty_like(logits)
+    for t in range(T):
+        if lib().orc_softmax32(N, _ptr(logits[t]), _ptr(out[t])) != 0:
+            raise ValueError("oracle softmax32: N must be 1..256")
     return out
 
 

@@ -84,6 +84,36 @@ void orc_sigmoid32_array(const float* in, float* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_sigmoid32(in[i]);
 }
 
+/* ---------------------------------------------------------------- softmax */
+
+/* Sum of slots [a, b) of v by recursive halving: the left half's sum plus
+ * the right half's, one fp32 add per node. */
+static float pairwise_sum32(const float* v, int a, int b) {
+  if (b - a == 1) return v[a];
+  const int mid = a + (b - a) / 2;
+  return pairwise_sum32(v, a, mid) + pairwise_sum32(v, mid, b);
+}
+
+/* p_i = e^{l_i} / sum_j e^{l_j} over the token's logits ([EVO] §ST-MoE), in
+ * fp32 with every step fixed (see moe_oracle.h): shifted by the largest
+ * logit, terms more than 64 below it set to 0, the sum a pairwise tree over
+ * 256 slots. */
+int orc_softmax32(int N, const float* logits, float* s) {
+  if (N < 1 || N > 256) return -1;
+  float m = logits[0];
+  for (int e = 1; e < N; ++e)
+    if (logits[e] > m) m = logits[e];
+  float E[256];
+  for (int e = 0; e < 256; ++e) E[e] = 0.0f;
+  for (int e = 0; e < N; ++e) {
+    const float x = logits[e] - m;
+    E[e] = (x < -64.0f) ? 0.0f : exp32_cw(x);
+  }
+  const float S = pairwise_sum32(E, 0, 256);
+  for (int e = 0; e < N; ++e) s[e] = E[e] / S;
+  return 0;
+}
+
 /* ---------------------------------------------------------------- logits */
 
 void orc_router_logits(int T, int H, int N, const void* x, int x_dtype,
@@ -120,6 +150,7 @@ int orc_route(const orc_route_cfg* c, const float* logits, const float* bias,
   if (c->topk_groups < 1 || c->topk_groups > G) return -1;
   if (k > c->topk_groups * gs) return -1;
   if (G > 1 && (c->group_topn < 1 || c->group_topn > gs)) return -1;
+  if (c->score_fn != ORC_SIGMOID && N > 256) return -1; /* orc_softmax32's domain */
 
   vi_t* ek = (vi_t*)malloc(sizeof(vi_t) * N);
   vi_t* gk = (vi_t*)malloc(sizeof(vi_t) * G);
@@ -138,16 +169,13 @@ int orc_route(const orc_route_cfg* c, const float* logits, const float* bias,
     for (int e = 0; e < N; ++e) se += exp((double)l[e] - m);
     lse[t] = m + log(se);
 
-    /* 1. scores */
-    for (int e = 0; e < N; ++e) {
-      if (c->score_fn == ORC_SIGMOID) {
-        s32[e] = orc_sigmoid32(l[e]);
-        s64[e] = (double)s32[e];
-      } else {
-        s64[e] = exp((double)l[e] - m) / se;
-        s32[e] = (float)s64[e];
-      }
+    /* 1. scores (fp32: they decide drops, and the gate is taken from them) */
+    if (c->score_fn == ORC_SIGMOID) {
+      for (int e = 0; e < N; ++e) s32[e] = orc_sigmoid32(l[e]);
+    } else {
+      orc_softmax32(N, l, s32);
     }
+    for (int e = 0; e < N; ++e) s64[e] = (double)s32[e];
     /* 2. keys */
     for (int e = 0; e < N; ++e) {
       float b = bias ? bias[e] : 0.0f;

@@ -50,6 +50,20 @@ extern "C" {
 float orc_sigmoid32(float l);
 void orc_sigmoid32_array(const float* in, float* out, int64_t n);
 
+/* fp32 softmax over one token's N logits (N <= 256), the score the v1/v2 gate
+ * takes and the drop order of device-level dropping is decided on ([EVO]
+ * §ST-MoE p_i(x); §DeepSeek-v2 device-level token dropping).  Definition
+ * (written independently on each side):
+ *   m   = the largest logit
+ *   E_e = the exponential of the sigmoid above applied to fl32(l_e - m),
+ *         except E_e = 0 when fl32(l_e - m) < -64
+ *   S   = pairwise sum of E over 256 slots (slots e >= N hold 0): the sum of
+ *         slots [a, b) is sum[a, (a+b)/2) + sum[(a+b)/2, b), down to single
+ *         slots, each + one correctly rounded fp32 add
+ *   s_e = E_e / S, correctly rounded fp32 divide.
+ * Returns -1 when N is outside 1..256. */
+int orc_softmax32(int N, const float* logits, float* s);
+
 /* Router logits l[t,e] = sum_h x[t,h] * Wg[e,h]  ([EVO] §ST-MoE z-loss: the
  * router's per-expert logits; [BUILD] §5.2 router is a linear layer).
  * x (typed) [T,H], wg (typed) [N,H]; out [T,N] fp64. */

@@ -38,30 +38,14 @@
 
 namespace moe {
 
-// Tile configuration of the three tile families (rows per tile = 16 * MB,
-// weight fragments prefetched PF steps ahead); overridable at build time.
-#ifndef MOE_FFN_BIG_MB
-#define MOE_FFN_BIG_MB 8
-#endif
-#ifndef MOE_FFN_BIG_PF
-#define MOE_FFN_BIG_PF 1
-#endif
-#ifndef MOE_FFN_MID_MB
-#define MOE_FFN_MID_MB 4
-#endif
-#ifndef MOE_FFN_MID_PF
-#define MOE_FFN_MID_PF 2
-#endif
-#ifndef MOE_FFN_SMALL_PF
-#define MOE_FFN_SMALL_PF 4
-#endif
-
-#ifndef MOE_FFN_SMALL_BPC
-#define MOE_FFN_SMALL_BPC 2  // workgroups per CU of the small-segment launch
-#endif
-#ifndef MOE_FFN_MINBLK
-#define MOE_FFN_MINBLK 2
-#endif
+// Tile configuration of the small-segment kernel's three tile families
+// (rows per tile = 16 * MB, weight fragments prefetched PF steps ahead) and
+// its occupancy (workgroups per CU).
+constexpr int kBigMB = 8, kBigPF = 1;    // >= 128 rows when the large-tile kernels cannot run
+constexpr int kMidMB = 4, kMidPF = 2;    // 32 .. 127 rows per segment
+constexpr int kSmallPF = 4;              // < 32 rows per segment (decode), 16-row tiles
+constexpr int kSmallBlocksPerCU = 2;
+constexpr int kMinBlocks = 2;            // launch bound of ffn_bf16_kernel
 
 constexpr int kBK = 64;        // k per pipeline step (8 chunks of 16 bytes)
 // Tiled weights: blocks of 16 rows x 32 k (1 KiB, kTileElems elements); the
@@ -321,7 +305,7 @@ __device__ __forceinline__ void run_tile(const TileCtx& c, int nmb, bf16_t* As) 
 }
 
 template <int MB, int PF, bool SWIGLU>
-__global__ __launch_bounds__(kThreads, MOE_FFN_MINBLK) void ffn_bf16_kernel(FfnLaunch a) {
+__global__ __launch_bounds__(kThreads, kMinBlocks) void ffn_bf16_kernel(FfnLaunch a) {
   constexpr int BM = 16 * MB;
   __shared__ __attribute__((aligned(16))) bf16_t As[2 * BM * kBK];
   __shared__ int tstart[kMaxSegs + 1];
@@ -368,11 +352,12 @@ __global__ __launch_bounds__(kThreads, MOE_FFN_MINBLK) void ffn_bf16_kernel(FfnL
 // =====================================================================
 // Large-segment kernel (prefill-sized segments, >= ~128 rows per expert).
 //
-// One workgroup per CU computes a 256-row x 256-weight-row tile with 4 waves
-// in a 2x2 layout.  Both operands stream global -> LDS with gfx950's direct
-// loads (global_load_lds_dwordx4), double buffered, so no registers stage
-// them; each wave then reads 16-byte MFMA fragments from LDS.  A wave owns
-// the 8 M-blocks of one parity (blocks 2j + wm), so a tile with fewer rows
+// One workgroup per CU computes a 256-row x 256-weight-row tile with 8 waves
+// (2 per SIMD) in a 2 x 4 layout: wave (wm, wn) = (wave & 1, wave >> 1).
+// Both operands stream global -> LDS with gfx950's direct buffer loads
+// (buffer_load_dwordx4 ... lds, see lds_dma.h), so no registers stage them;
+// each wave then reads 16-byte MFMA fragments from LDS.  A wave owns the
+// M-blocks of one parity (blocks 2j + wm), so a tile with fewer rows
 // shortens every wave's work equally.  Row splits of a segment are balanced
 // (ceil(rows / tiles) rows each), so the tiles that share an expert's
 // weights cost the same and stream them through L2 together.
@@ -631,7 +616,10 @@ __device__ __forceinline__ BigLoads big_loads(const FfnGroup& g, const BigTile& 
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int q = 4 * p + (wave >> 1);  // row block of the tile; gate/up: 8.. are the up half
-    const int wr = (SWIGLU && q >= 8) ? g.up_off + col0 + 16 * (q - 8) : col0 + 16 * q;
+    // columns past n_out (never stored) read block 0, so the offset, which
+    // the buffer's range check does not cover, stays inside the expert
+    const int c = col0 + 16 * ((SWIGLU && q >= 8) ? q - 8 : q);
+    const int wr = ((SWIGLU && q >= 8) ? g.up_off : 0) + (c < g.n_out ? c : 0);
     L.bsoff[p] = wave_uniform(static_cast<uint32_t>(wr) * krow_bytes);
   }
   L.rows_needed = 2 * t.nmbw * 16;  // tile rows any wave reads
@@ -875,11 +863,16 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   }
   // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
   // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
-  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.
+  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.  A
+  // block whose columns lie past n_out (their results are never stored)
+  // reads block 0 instead, so every address stays inside the expert's
+  // weights (the buffer's range check covers the per-lane offset only).
   const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const uint32_t boff =
-      static_cast<uint32_t>((SWIGLU ? nt * 128 : nt * 256) + wave * 16) * krow_bytes + lane * 16u;
-  const uint32_t bsoff1 = static_cast<uint32_t>(SWIGLU ? g.up_off : 128) * krow_bytes;
+  const int col0 = (SWIGLU ? nt * 128 : nt * 256) + wave * 16;
+  const int c0 = col0 < g.n_out ? col0 : 0;
+  const int c1 = SWIGLU ? g.up_off + c0 : (col0 + 128 < g.n_out ? col0 + 128 : 0);
+  const uint32_t boff0 = static_cast<uint32_t>(c0) * krow_bytes + lane * 16u;
+  const uint32_t boff1 = static_cast<uint32_t>(c1) * krow_bytes + lane * 16u;
 
   // k-steps step, step + 1 (step even)
   auto issue_a = [&](int step, bf16_t* Xb) {
@@ -890,8 +883,8 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   };
   auto issue_w = [&](int step, bf16_t* Bb) {
     const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
-    dma16(rb, boff, kw, Bb + wave * kTileElems);
-    dma16(rb, boff, bsoff1 + kw, Bb + (8 + wave) * kTileElems);
+    dma16(rb, boff0, kw, Bb + wave * kTileElems);
+    dma16(rb, boff1, kw, Bb + (8 + wave) * kTileElems);
   };
   // activation loads of this wave per pair of k-steps: NA0, one more with
   // `extra`
@@ -1130,7 +1123,6 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
     k128 = k128 && fl.g[i].K % 128 == 0;
     klong = klong && fl.g[i].K >= 1024;
   }
-#ifndef MOE_FFN_NO_PP
   // Measured (V3 prefill: gate/up K = 7168, down K = 2048; v1 and v2:
   // gate/up K = 2048, down K = 1408): every one of these phases runs faster
   // on the ping-pong kernel (v1 down 0.264 -> 0.238 ms, v2 down 0.331 ->
@@ -1143,7 +1135,6 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
       ffn_pp_kernel<false><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
     return hipGetLastError();
   }
-#endif
   if (phase == 0)
     ffn_big_kernel<true><<<static_cast<int>(grid), kBigThreads, 0, st>>>(fl);
   else
@@ -1160,15 +1151,13 @@ hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int r
     const int cols = phase == 0 ? 128 : 256;
     fl.nt[i] = (groups[i].n_out + cols - 1) / cols;
   }
-#ifndef MOE_FFN_NO_BIG
   bool big_ok = true;  // buffer addressing needs 32-bit byte offsets
   for (int i = 0; i < ngroups; ++i)
     big_ok = big_ok && groups[i].a_bytes != 0 && groups[i].w_bytes != 0 && groups[i].o_bytes != 0;
   if (rows_hint >= 128 && big_ok) return launch_big(fl, phase, st);
-#endif
-  if (rows_hint >= 128) return launch_mb<MOE_FFN_BIG_MB, MOE_FFN_BIG_PF>(fl, phase, MOE_FFN_MINBLK, st);
-  if (rows_hint >= 32) return launch_mb<MOE_FFN_MID_MB, MOE_FFN_MID_PF>(fl, phase, 2, st);
-  return launch_mb<1, MOE_FFN_SMALL_PF>(fl, phase, MOE_FFN_SMALL_BPC, st);
+  if (rows_hint >= 128) return launch_mb<kBigMB, kBigPF>(fl, phase, kMinBlocks, st);
+  if (rows_hint >= 32) return launch_mb<kMidMB, kMidPF>(fl, phase, 2, st);
+  return launch_mb<1, kSmallPF>(fl, phase, kSmallBlocksPerCU, st);
 }
 
 // ================================================================ weight packing

@@ -49,11 +49,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -77,17 +72,16 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// ------------------------------------------------------------------ fp32 sigmoid
-// The score every selection is made on, so it is defined exactly:
-//   x = clamp(-l, -87, 87); n = rne(fl32(x * log2 e));
+// ------------------------------------------------------------------ fp32 exponential
+// e^x for x in [-87, 87], defined exactly so that every score a selection or
+// a drop is decided on is reproducible bit for bit:
+//   n = rne(fl32(x * log2 e));
 //   r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r)     (Cody & Waite, with
 //       fdlibm's two-part ln 2);
-//   p = sum_{j<=7} r^j/j! by fma Horner; E = p * 2^n; s = 1 / (1 + E)
-// with correctly rounded fp32 add and divide.  The clamp keeps every result
-// a normal fp32 number (s saturates at sigma(-87) below l = -87).
-__device__ __forceinline__ float sigmoid_score(float l) {
+//   p = sum_{j<=7} r^j/j! by fma Horner; E = p * 2^n.
+// For |x| <= 87 the result is a normal fp32 number.
+__device__ __forceinline__ float exp32_cw(float x) {
 #pragma clang fp contract(off)
-  float x = __builtin_fminf(__builtin_fmaxf(-l, -87.0f), 87.0f);
   const float n = __builtin_rintf(x * 0x1.715476p+0f);
   float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
   r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
@@ -99,9 +93,39 @@ __device__ __forceinline__ float sigmoid_score(float l) {
   p = __builtin_fmaf(p, r, 0.5f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  const float e = __builtin_ldexpf(p, static_cast<int>(n));
-  const float d = 1.0f + e;
+  return __builtin_ldexpf(p, static_cast<int>(n));
+}
+
+// fp32 sigmoid s = 1 / (1 + exp32_cw(clamp(-l, -87, 87))), correctly rounded
+// add and divide.  The clamp keeps every result a normal fp32 number (s
+// saturates at sigma(-87) below l = -87).
+__device__ __forceinline__ float sigmoid_score(float l) {
+#pragma clang fp contract(off)
+  const float x = __builtin_fminf(__builtin_fmaxf(-l, -87.0f), 87.0f);
+  const float d = 1.0f + exp32_cw(x);
   return 1.0f / d;
+}
+
+// Softmax numerator of a logit l given the token's largest logit m:
+// exp32_cw(l - m), and exactly 0 when l - m < -64 (such a term is below
+// 2^-92 of the largest one, and the quotient by the sum, at most 256, stays a
+// normal fp32 number for every term that is kept).
+__device__ __forceinline__ float softmax_numerator(float l, float m) {
+#pragma clang fp contract(off)
+  const float x = l - m;
+  return x < -64.0f ? 0.0f : exp32_cw(x);
+}
+
+// Sum over the 64 lanes by recursive halving in index order: after the step
+// with offset o every lane holds the sum of its aligned block of 2o lanes,
+// formed as (lower half) + (upper half).  With lane L holding the sum of
+// entries 4L .. 4L+3 as (e0 + e1) + (e2 + e3), the result is the pairwise
+// sum of 256 entries (a binary tree over index halves), the same on every
+// lane.
+__device__ __forceinline__ float wave_sum_pairwise_f32(float v) {
+#pragma unroll
+  for (int o = 1; o <= 32; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
 }
 
 // ------------------------------------------------------------------ launchers

@@ -413,12 +413,19 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
         f32x4{l[0], l[1], l[2], l[3]};
   }
 
-  // log-sum-exp over the N logits
+  // softmax numerators E_e = e^(l_e - m) and their sum S, both defined
+  // exactly (exp32_cw, terms under e^-64 of the largest are 0; S is the
+  // pairwise sum over the 256 expert slots, empty slots 0), so the softmax
+  // score E_e / S is reproducible bit for bit; S also gives the
+  // log-sum-exp of the z-loss.
   float m = valid ? fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])) : -INFINITY;
   m = wave_max_f32(m);
-  float se = 0.f;
-  if (valid) se = __expf(l[0] - m) + __expf(l[1] - m) + __expf(l[2] - m) + __expf(l[3] - m);
-  se = wave_sum_f32(se);
+  float ex[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ex[r] = softmax_numerator(l[r], m);
+  }
+  const float se = wave_sum_pairwise_f32((ex[0] + ex[1]) + (ex[2] + ex[3]));
   const float lse = m + __logf(se);
 
   // scores and selection keys
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
     if (p.score_fn == MOE_SCORE_SIGMOID) {
       s[r] = sigmoid_score(l[r]);
     } else {
-      s[r] = __expf(l[r] - m) / se;
+      s[r] = ex[r] / se;
     }
     float b = (valid && p.bias) ? p.bias[e0 + r] : 0.0f;
     float base = (p.score_fn == MOE_SCORE_SIGMOID) ? s[r] : l[r];

@@ -1,7 +1,12 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (moe_layer_forward with the default tiles): routing,
-dispatch and statistics over every token, layer outputs on sampled tokens
-the oracle computes one by one."""
+dispatch and statistics over every token; layer outputs on every token of
+the decode layer and, for the larger layers, on a stratified sample (the
+first and last row of every row tile of every expert segment, every
+shared-expert tile, tokens with dropped slots) that the oracle computes one
+by one, the calls spread over the host cores."""
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -10,9 +15,8 @@ import oracle
 from routing_expert_ffn_sigmoid_amd import workloads
 
 from gpu_common import (F32_MAXREL, check_dispatch, check_outputs, check_routing, check_seq_stats,
-                        check_stats,
-                        f64, gpu, layer_forward, make_inputs, normwise, oracle_rows,
-                        require_gpu, say, typed)
+                        check_stats, gpu, layer_forward, make_inputs, normwise, oracle_rows,
+                        oracle_workers, require_gpu, say, stratified_tokens, typed)
 
 pytestmark = gpu
 
@@ -34,31 +38,34 @@ def _logit_sample_check(inp, aux, tokens):
     assert mr <= F32_MAXREL, f"router logits max-rel {mr}"
 
 
-def _run(wl, inp, n_sample, pick_dropped=False):
+def _run(wl, inp, min_tokens, all_tokens=False):
+    """The layer at full size: routing, dispatch and statistics over every
+    token; outputs on every token (all_tokens) or on a stratified sample
+    that reaches the first and last row of every row tile of every expert
+    segment, every shared-expert tile and tokens with dropped slots."""
     say(f"layer {wl.name}")
     out, aux = layer_forward(wl, inp)
     r = check_routing(wl, aux, inp["bias"])
     d = check_dispatch(wl, aux, r)
     st = check_stats(wl, aux)
-    rng = np.random.default_rng(0)
-    toks = sorted(rng.choice(wl.T, size=min(n_sample, wl.T), replace=False).tolist())
-    if pick_dropped:
-        dropped = np.nonzero((d["inv_row"] < 0).any(axis=1))[0]
-        if dropped.size:
-            toks = sorted(set(toks[: n_sample // 2]) | set(dropped[: n_sample - n_sample // 2].tolist()))
-    _logit_sample_check(inp, aux, toks)
+    toks = list(range(wl.T)) if all_tokens else stratified_tokens(wl, d, min_count=min_tokens)
+    _logit_sample_check(inp, aux, toks[:: max(1, len(toks) // 64)])
+    t0 = time.perf_counter()
     ref = oracle_rows(wl, inp, r, d, toks)
+    dt = time.perf_counter() - t0
     mr, l2 = check_outputs(wl, out, ref, toks)
-    say(f"  sampled {len(toks)} tokens: max-rel {mr:.2e} rel-L2 {l2:.2e}; L_B {st['L_B']:.4f} "
-        f"dropped {d['n_dropped']}")
-    return out, aux, d
+    n_drop_tok = int(((d["inv_row"][toks] < 0).any(axis=1)).sum())
+    say(f"  {len(toks)} tokens ({n_drop_tok} with a dropped slot) against the oracle in "
+        f"{dt:.1f} s on {oracle_workers()} host threads: max-rel {mr:.2e} rel-L2 {l2:.2e}; "
+        f"L_B {st['L_B']:.4f} dropped {d['n_dropped']}")
+    return out, aux, d, toks
 
 
 def test_v1_shaped_layer():
     require_gpu()
     wl = workloads.V1
     inp = make_inputs(wl)
-    _run(wl, inp, 24)
+    _run(wl, inp, 128)
 
 
 def test_v2_shaped_layer_device_limited_with_device_drop():
@@ -67,8 +74,9 @@ def test_v2_shaped_layer_device_limited_with_device_drop():
     require_gpu()
     wl = workloads.V2
     inp = make_inputs(wl)
-    _, _, d = _run(wl, inp, 24, pick_dropped=True)
+    _, _, d, toks = _run(wl, inp, 128)
     assert d["n_dropped"] > 0
+    assert (d["inv_row"][toks] < 0).any()
 
 
 def test_v3_prefill_layer(v3_weights):
@@ -76,7 +84,8 @@ def test_v3_prefill_layer(v3_weights):
     from routing_expert_ffn_sigmoid_amd import synth
     inp = dict(v3_weights)
     inp["x"] = synth.normal((wl.T, wl.H), wl.x_std, torch.bfloat16, "cuda", wl.seed, f"x_T{wl.T}")
-    _, aux, _ = _run(wl, inp, 6)
+    _, aux, _, toks = _run(wl, inp, 256)
+    assert len(toks) >= 256
     # the batch as four sequences of 2048 tokens (sequence-wise statistics)
     ref = check_seq_stats(wl, [0, 2048, 4096, 6144, 8192], aux["topk_idx"], aux["token_lse"],
                           aux["logits"])
@@ -88,7 +97,7 @@ def test_v3_decode_layer(v3_weights):
     from routing_expert_ffn_sigmoid_amd import synth
     inp = dict(v3_weights)
     inp["x"] = synth.normal((wl.T, wl.H), wl.x_std, torch.bfloat16, "cuda", wl.seed, f"x_T{wl.T}")
-    _run(wl, inp, 6)
+    _run(wl, inp, 0, all_tokens=True)
 
 
 def test_v3_skew_layer_with_capacity(v3_weights):
@@ -97,7 +106,8 @@ def test_v3_skew_layer_with_capacity(v3_weights):
     inp = dict(v3_weights)
     inp["x"] = synth.normal((wl.T, wl.H), wl.x_std, torch.bfloat16, "cuda", wl.seed, f"x_T{wl.T}")
     inp["bias"] = synth.zipf_bias(wl.N, wl.bias_param, "cuda", wl.seed)
-    out, aux, d = _run(wl, inp, 6, pick_dropped=True)
+    out, aux, d, toks = _run(wl, inp, 512)
     assert wl.capacity == 640
-    assert d["n_dropped"] > 0
+    assert d["n_dropped"] > 0 and len(toks) >= 512
+    assert int(((d["inv_row"][toks] < 0).any(axis=1)).sum()) >= min(64, d["n_tok_all_dropped"] + 1)
     assert int(np.max(np.diff(d["offsets"]))) <= wl.capacity

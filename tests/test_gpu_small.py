@@ -49,6 +49,31 @@ def test_sigmoid_scores_bit_identical_to_oracle_on_a_sweep():
     np.testing.assert_array_equal(g["topk_score"].cpu().numpy(), r["topk_score"])
 
 
+@pytest.mark.parametrize("N,k", [(64, 64), (160, 64), (256, 64), (16, 16), (4, 4)])
+def test_softmax_scores_bit_identical_to_oracle(N, k):
+    """The fp32 softmax (exact exponential, terms 64 below the maximum set
+    to 0, pairwise sum over 256 slots, correctly rounded divide) on the GPU
+    and in the oracle, bit for bit: the k largest scores of each token at
+    logit scales from 0.05 to 40 (the largest cross the cut-off), with ties
+    and a token of equal logits."""
+    require_gpu()
+    rng = np.random.default_rng(N + k)
+    T = 4096
+    scale = rng.choice([0.05, 0.5, 2.0, 8.0, 40.0], size=(T, 1)).astype(np.float32)
+    logits = (rng.standard_normal((T, N)).astype(np.float32) * scale).astype(np.float32)
+    logits[:64] = np.round(logits[:64])  # ties
+    logits[64] = 1.25                    # all equal
+    wl = workloads.TINY.with_(T=T, N=N, k=k, n_groups=1, topk_groups=1,
+                              score_fn=workloads.SOFTMAX, norm_topk=0)
+    say(f"softmax scores N={N} k={k}")
+    g = _route_only(wl, torch.from_numpy(logits).cuda(), None)
+    r = oracle_route(wl, logits, None)
+    np.testing.assert_array_equal(g["topk_idx"].cpu().numpy(), r["topk_idx"])
+    np.testing.assert_array_equal(g["topk_score"].cpu().numpy(), r["topk_score"])
+    mr, _ = normwise(g["token_lse"].cpu().numpy(), r["lse"])
+    assert mr <= F32_MAXREL, f"lse max-rel {mr}"
+
+
 @pytest.mark.parametrize("G,keep,k,topn", [(4, 2, 4, 2), (4, 1, 3, 1), (2, 1, 5, 2), (1, 1, 6, 2)])
 @pytest.mark.parametrize("fn", [workloads.SIGMOID, workloads.SOFTMAX])
 def test_route_ties_match_oracle(G, keep, k, topn, fn):

@@ -91,8 +91,11 @@ def test_dense_mixture_k_equals_N():
     r = oracle.route(logits, None, N, 1, 1, 2, oracle.SOFTMAX, 0, 1.0)
     d = oracle.dispatch(r["topk_idx"], r["topk_score"], N, 0)
     assert d["offsets"][-1] == T * N
-    p = np.exp(logits.astype(np.float64) - logits.max(1, keepdims=True))
-    p /= p.sum(1, keepdims=True)
+    # the gates are the fp32 softmax scores (pinned against the fp64 softmax
+    # in test_oracle_softmax.py); the mixture identity is checked on them
+    p = oracle.softmax32(logits).astype(np.float64)
+    p64 = np.exp(logits.astype(np.float64) - logits.max(1, keepdims=True))
+    np.testing.assert_allclose(p, p64 / p64.sum(1, keepdims=True), rtol=2e-6)
     for t in range(T):
         sel = r["topk_idx"][t]
         out = oracle.token_output(x[t], [w13[e] for e in sel], [w2[e] for e in sel],
@@ -189,3 +192,38 @@ def test_combine_matches_numpy_gather_sum():
                 ref[t] += g[t, j] * y[inv[t, j]].astype(np.float64)
     np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(oracle.combine(y, None, inv, g), ref - ysh, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fn", [oracle.SIGMOID, oracle.SOFTMAX])
+def test_combine_of_expert_rows_equals_token_output(fn):
+    """The layer computed the way the GPU path factors it -- dispatch, one
+    SwiGLU row per kept (token, expert) assignment in the dispatch's row
+    order, the shared expert per token, then the combine -- equals the
+    per-token definition (shared output plus gate-weighted routed outputs,
+    dropped slots contributing nothing).  The rows are rounded to fp32 once
+    before the combine, hence the 1e-6 tolerance."""
+    rng = np.random.default_rng(15)
+    T, H, I, N, k, C = 12, 16, 8, 6, 2, 3
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w13 = (0.3 * rng.standard_normal((N, 2 * I, H))).astype(np.float32)
+    w2 = (0.3 * rng.standard_normal((N, H, I))).astype(np.float32)
+    ws13 = (0.3 * rng.standard_normal((2 * I, H))).astype(np.float32)
+    ws2 = (0.3 * rng.standard_normal((H, I))).astype(np.float32)
+    logits = rng.standard_normal((T, N)).astype(np.float32)
+    r = oracle.route(logits, None, k, 1, 1, 2, fn, 1, 1.5)
+    d = oracle.dispatch(r["topk_idx"], r["topk_score"], N, C)
+    assert d["n_dropped"] > 0
+    M = int(d["offsets"][-1])
+    seg = np.searchsorted(d["offsets"], np.arange(M), side="right") - 1
+    y = np.stack([oracle.swiglu_row(x[d["row_token"][q]], w13[seg[q]], w2[seg[q]])
+                  for q in range(M)]).astype(np.float32)
+    ysh = np.stack([oracle.swiglu_row(x[t], ws13, ws2) for t in range(T)]).astype(np.float32)
+    got = oracle.combine(y, ysh, d["inv_row"], r["topk_gate"])
+    for t in range(T):
+        keep = d["inv_row"][t] >= 0
+        sel = r["topk_idx"][t]
+        ref = oracle.token_output(x[t], [w13[e] if kp else None for e, kp in zip(sel, keep)],
+                                  [w2[e] if kp else None for e, kp in zip(sel, keep)],
+                                  r["topk_gate"][t], ws13, ws2, 1, I, I)
+        err = np.max(np.abs(got[t] - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-6, (t, err)

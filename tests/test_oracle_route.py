@@ -175,9 +175,10 @@ def test_route_invariants_random(N, G, keep, k, fn, norm, scale):
     if norm:
         np.testing.assert_allclose(g.sum(axis=1), scale, rtol=1e-12)
     else:
+        # the fp32 softmax score (within its error bound of the fp64 one)
         ref = np.exp(logits.astype(np.float64) - logits.max(1, keepdims=True))
         ref /= ref.sum(1, keepdims=True)
-        np.testing.assert_allclose(g, np.take_along_axis(ref, idx, 1) * scale, rtol=1e-12)
+        np.testing.assert_allclose(g, np.take_along_axis(ref, idx, 1) * scale, rtol=2e-6)
     # the bias changes the selection only: z and P do not depend on it
     r0 = oracle.route(logits, None, k, G, keep, 2, fn, norm, scale)
     np.testing.assert_array_equal(r0["lse"], r["lse"])
@@ -187,9 +188,11 @@ def test_route_invariants_random(N, G, keep, k, fn, norm, scale):
     st0 = oracle.load_stats(logits, d0["counts"], k, fn)
     np.testing.assert_array_equal(st0["P"], st1["P"])
     assert st0["z"] == st1["z"]
-    # unnormalised gate = unbiased score of the chosen expert
-    if fn == oracle.SIGMOID:
-        np.testing.assert_array_equal(r["topk_score"], np.take_along_axis(s, idx, 1))
+    # the reported score is the unbiased score of the chosen expert
+    s_all = s if fn == oracle.SIGMOID else oracle.softmax32(logits)
+    np.testing.assert_array_equal(r["topk_score"], np.take_along_axis(s_all, idx, 1))
+    if not norm:
+        np.testing.assert_array_equal(g, r["topk_score"].astype(np.float64) * scale)
 
 
 @pytest.mark.parametrize("fn", [oracle.SIGMOID, oracle.SOFTMAX])
