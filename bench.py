@@ -2,7 +2,7 @@
 combine + load statistics) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--cpu-sample S]
+                    [--no-cpu-baseline] [--cpu-sample S] [--no-extra]
 
 Default workload: the V3-shaped prefill layer (T=8192 tokens, hidden 7168,
 256 routed SwiGLU experts of width 2048 in 8 groups, keep 4 groups, top-8,
@@ -14,8 +14,14 @@ everything already resident.
 Prints one JSON line.  `value` = tokens/s of the whole layer.  `roofline`
 describes the dominant kernel (the SwiGLU gate/up grouped GEMM), timed with
 HIP events recorded on the launch stream around that stage in every timed
-step.  `cpu_baseline` is the single-threaded C oracle on a bounded sample of
-tokens of the same workload.
+step.  `layer` gives the whole layer's MFMA fraction and the median, min and
+max step time from the same events.  For the V3 prefill workload the line
+also carries `decode` (T = 128) and `skew` (T = 16384, capacity 640)
+objects: the same layer and weights timed in the same process.  `clocks`
+samples the graphics clock during the timed loop, `environment` names the
+GPU, ROCm, torch and host CPU, and `wave_placement` checks the SIMD pairing
+the prefill GEMM schedule relies on.  `cpu_baseline` is the single-threaded
+C oracle on a bounded sample of tokens of the same workload.
 """
 from __future__ import annotations
 
@@ -91,34 +97,75 @@ def algorithmic_work(wl, kept_rows: int) -> dict:
     }
 
 
-def source_digest(paths) -> str:
-    h = hashlib.sha256()
-    for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+LIB_PATH = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "libmoe.so")
+GATE_UP_KERNEL = "ffn_pp_kernel"
 
 
-def load_traffic(kernel_src: str, workload: str):
+def code_object_digest(kernel: str, lib_path: str = LIB_PATH):
+    """sha256 (16 hex digits) of the gfx950 code object in libmoe.so that
+    holds `kernel`: the device code a counter record was taken on.  The
+    library's .hip_fatbin section holds one clang offload bundle per
+    translation unit; each bundle lists its entries (offset, size, target
+    triple)."""
+    import struct
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def section(i):
+        name, _t, _f, _a, off, size = struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize)
+        return name, off, size
+
+    stroff = section(shstrndx)[1]
+    fatbin = None
+    for i in range(shnum):
+        name, off, size = section(i)
+        if data[stroff + name:data.index(b"\0", stroff + name)] == b".hip_fatbin":
+            fatbin = data[off:off + size]
+    if fatbin is None:
+        return None
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    p = fatbin.find(magic)
+    while p >= 0:
+        n = struct.unpack_from("<Q", fatbin, p + len(magic))[0]
+        q = p + len(magic) + 8
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", fatbin, q)
+            triple = fatbin[q + 24:q + 24 + tlen]
+            q += 24 + tlen
+            co = fatbin[p + off:p + off + size]
+            if triple.endswith(b"gfx950") and kernel.encode() in co:
+                return hashlib.sha256(co).hexdigest()[:16]
+        p = fatbin.find(magic, p + 1)
+    return None
+
+
+def load_traffic(workload: str):
     """Measured HBM bytes per launch of the gate/up kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    rocprofv3 counter summary, if it was taken on the device code this
+    library holds (same code object digest)."""
     path = os.path.join(ROOT, "profiles", f"ffn_gate_up_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != source_digest([kernel_src]):
+    cur = code_object_digest(GATE_UP_KERNEL)
+    if cur is None or rec.get("code_object_digest") != cur:
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, logits_gpu, sample: int) -> dict:
+def cpu_baseline(wl, inp, sample: int) -> dict:
     """The C oracle (one thread) on `sample` tokens of the workload: router
-    logits, routing, dispatch and the layer output of each sampled token."""
+    logits, routing, dispatch and the layer output of each sampled token.
+    An untimed first pass finds the experts the oracle's own routing picks,
+    so their weights are on the host before the timed pass."""
     import numpy as np
     import torch
 
     import oracle
+    from routing_expert_ffn_sigmoid_amd import workloads
 
     def typed(t):
         t = t.detach().contiguous().cpu()
@@ -131,10 +178,19 @@ def cpu_baseline(wl, inp, logits_gpu, sample: int) -> dict:
     wg = typed(inp["w_router"])
     bias = inp["bias"].cpu().numpy() if inp["bias"] is not None else None
     fn = oracle.SIGMOID if wl.score_fn == 1 else oracle.SOFTMAX
-    # the weights the sampled tokens need, copied to host before timing
-    lg = logits_gpu[toks].cpu().numpy()
-    r0 = oracle.route(lg, bias, wl.k, wl.n_groups, wl.topk_groups, wl.group_topn, fn,
-                      wl.norm_topk, wl.route_scale)
+    gcap = workloads.group_capacity_for(wl) if wl.group_capacity else 0
+
+    def route_dispatch():
+        logits = oracle.router_logits(x, wg).astype(np.float32)
+        r = oracle.route(logits, bias, wl.k, wl.n_groups, wl.topk_groups, wl.group_topn, fn,
+                         wl.norm_topk, wl.route_scale)
+        if gcap > 0:
+            d = oracle.dispatch_grouped(r["topk_idx"], r["topk_score"], wl.N, wl.n_groups, gcap)
+        else:
+            d = oracle.dispatch(r["topk_idx"], r["topk_score"], wl.N, wl.capacity)
+        return r, d
+
+    r0, _ = route_dispatch()
     experts = sorted(set(int(e) for e in r0["topk_idx"].ravel()))
     w13 = {e: typed(inp["w13"][e]) for e in experts}
     w2 = {e: typed(inp["w2"][e]) for e in experts}
@@ -142,22 +198,21 @@ def cpu_baseline(wl, inp, logits_gpu, sample: int) -> dict:
     ws2 = typed(inp["ws2"]) if inp.get("ws2") is not None else None
 
     t0 = time.perf_counter()
-    logits = oracle.router_logits(x, wg).astype(np.float32)
-    r = oracle.route(logits, bias, wl.k, wl.n_groups, wl.topk_groups, wl.group_topn, fn,
-                     wl.norm_topk, wl.route_scale)
-    d = oracle.dispatch(r["topk_idx"], r["topk_score"], wl.N, wl.capacity)
+    r, d = route_dispatch()
+    done = 0
     for i in range(len(toks)):
-        sel = [int(e) for e in r["topk_idx"][i]]
-        a13 = [w13.get(e) if d["inv_row"][i, j] >= 0 else None for j, e in enumerate(sel)]
-        a2 = [w2.get(e) if d["inv_row"][i, j] >= 0 else None for j, e in enumerate(sel)]
-        if any(a is None and d["inv_row"][i, j] >= 0 for j, a in enumerate(a13)):
-            continue  # fp32 rounding of the oracle's own logits chose an uncopied expert
-        oracle.token_output(x[i], a13, a2, r["topk_gate"][i], ws13, ws2, wl.n_shared,
-                            wl.I_shared, wl.I)
+        sel = [int(e) if d["inv_row"][i, j] >= 0 else None for j, e in enumerate(r["topk_idx"][i])]
+        if any(e is not None and e not in w13 for e in sel):
+            continue  # cannot happen: the timed routing repeats the first pass
+        oracle.token_output(x[i], [w13[e] if e is not None else None for e in sel],
+                            [w2[e] if e is not None else None for e in sel], r["topk_gate"][i],
+                            ws13, ws2, wl.n_shared, wl.I_shared, wl.I)
+        done += 1
     dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(toks)} tokens of {wl.name}: router logits, routing, dispatch and "
-                      f"the layer output of each, single-threaded C, {dt:.1f} s"}
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(toks)} tokens of {wl.name} ({done} computed, "
+                      f"{len(toks) - done} skipped): router logits, routing, dispatch and the "
+                      f"layer output of each, single-threaded C, {dt:.1f} s"}
 
 
 COPY_BYTES = 1 << 30
@@ -247,24 +302,178 @@ def summarize_profile(d: str, workload: str, commands: dict):
                or ("ffn" in k and "<" in k and "true" in k[k.find("<"):])]
     if gate_up:
         k = max(gate_up, key=lambda n: avg.get(n, 0.0))
-        src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")
         rec = {"kernel": k, "workload": workload, "bytes_per_launch": traffic[k],
                "fetch_kib": fetch.get(k), "write_kib": write.get(k),
                "fetch_scale": f_scale, "write_scale": w_scale,
-               "avg_launch_us": avg.get(k), "source_digest": source_digest([src]),
+               "avg_launch_us": avg.get(k), "code_object_digest": code_object_digest(GATE_UP_KERNEL),
                "commands": commands}
         with open(os.path.join(ROOT, "profiles", f"ffn_gate_up_traffic_{workload}.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
     print("\n".join(lines))
 
 
+class ClockSampler:
+    """Samples the GPU's current graphics clock (amdsmi) from a host thread
+    while a timed loop runs; nothing is sent to the GPU's queues."""
+
+    def __init__(self, period_s: float = 0.005):
+        self.period = period_s
+        self.samples = []
+        self.handle = None
+        self.thread = None
+        self.stop = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            dev = int(os.environ.get("HIP_VISIBLE_DEVICES", "0").split(",")[0] or 0)
+            self.handle = handles[0 if len(handles) == 1 else dev]
+            self.amdsmi = amdsmi
+        except Exception:  # no SMI access: clocks are reported as null
+            self.handle = None
+
+    def _run(self):
+        while not self.stop:
+            try:
+                info = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
+                self.samples.append(float(info["clk"]))
+            except Exception:
+                return
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+        self.samples = []
+        self.stop = False
+        if self.handle is not None:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        if self.thread is not None:
+            self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"sclk_mhz_mean": round(sum(v) / len(v), 1), "sclk_mhz_min": v[0],
+                "sclk_mhz_max": v[-1], "samples": len(v)}
+
+
+def environment(torch) -> dict:
+    env = {"gpu": torch.cuda.get_device_name(0)}
+    try:
+        env["max_sclk_mhz"] = torch.cuda.get_device_properties(0).clock_rate // 1000
+    except Exception:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    env["torch"] = torch.__version__
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    env["host_cpu"] = cpu
+    try:
+        env["host_threads"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        env["host_threads"] = os.cpu_count()
+    return env
+
+
+def wave_placement(moe, torch) -> dict:
+    """Whether waves w and w + 4 of a large-tile workgroup share a SIMD on
+    this GPU (the ping-pong GEMM schedule is fastest when they do)."""
+    n = 256
+    simd = torch.full((n, 8), -1, dtype=torch.int32, device="cuda")
+    moe.moe_probe_wave_simd(n, simd)
+    torch.cuda.synchronize()
+    s = simd.cpu().tolist()
+    ok = sum(1 for g in s if all(g[w] == g[w + 4] for w in range(4)) and len(set(g[:4])) == 4)
+    return {"workgroups": n, "w_and_w_plus_4_share_simd": ok, "example": s[0]}
+
+
+def time_layer(moe, torch, wl, inp, weights, steps: int, warmup: int, sampler=None) -> dict:
+    """Warm up, then run `steps` calls of moe_layer_forward bracketed by
+    synchronisations; per-stage and per-step times from HIP events recorded
+    by the library on the launch stream."""
+    cfg = moe.make_cfg(wl)
+    ws = moe.alloc_workspace(cfg, device="cuda")
+    aux = moe.alloc_aux(cfg, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16 if wl.act_dtype == 1 else torch.float32,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        moe.moe_layer_forward(cfg, weights, inp["x"], inp["bias"], out, aux, ws,
+                              stage_events=events, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    ns = moe.N_STAGES + 1
+    evs = hev.create(steps * ns)
+    torch.cuda.synchronize()
+    if sampler is not None:
+        sampler.__enter__()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i * ns:(i + 1) * ns])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if sampler is not None:
+        sampler.__exit__(None, None, None)
+    stage_ms = [0.0] * moe.N_STAGES
+    step_ms = []
+    for i in range(steps):
+        base = i * ns
+        for s_ in range(moe.N_STAGES):
+            stage_ms[s_] += hev.elapsed_ms(evs[base + s_], evs[base + s_ + 1]) / steps
+        step_ms.append(hev.elapsed_ms(evs[base], evs[base + ns - 1]))
+    hev.destroy(evs)
+    step_ms.sort()
+    res = {
+        "ms_per_step": elapsed * 1e3 / steps,
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                    "max": round(step_ms[-1], 4)},
+        "stage_ms": dict(zip(moe.STAGES, stage_ms)),
+        "kept": int(aux["offsets"][-1].item()),
+        "touched": int((aux["counts"] > 0).sum().item()),
+        "n_dropped": [int(v) for v in aux["n_dropped"].cpu().tolist()],
+        "aux": aux,
+    }
+    del ws, out
+    return res
+
+
+def touched_weight_bytes(wl, touched: int) -> int:
+    wsz = 2 if wl.w_dtype == 1 else 4
+    rsz = 2 if wl.router_dtype == 1 else 4
+    return (touched * 3 * wl.I * wl.H * wsz + 3 * wl.n_shared * wl.I_shared * wl.H * wsz
+            + wl.N * wl.H * rsz)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the decode and skew sub-measurements of the V3 prefill run")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
@@ -276,8 +485,8 @@ def main():
         return
     if args.summarize_profile:
         cmd = "rocprofv3 {opt} -d <dir> -o run --output-format csv -- python3 bench.py {args}"
-        run = f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline"
-        pmc = f"--workload {args.workload} --steps 2 --warmup 1 --no-cpu-baseline"
+        run = f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-extra"
+        pmc = f"--workload {args.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extra"
         commands = {"trace": cmd.format(opt="--kernel-trace --stats", args=run),
                     "fetch": cmd.format(opt="--pmc FETCH_SIZE", args=pmc),
                     "write": cmd.format(opt="--pmc WRITE_SIZE", args=pmc),
@@ -300,55 +509,26 @@ def main():
     dev = "cuda"
     print(f"[bench] workload {wl.name}: generating inputs in HBM", file=sys.stderr, flush=True)
     inp = synth.make_inputs(wl, device=dev)
-    cfg = moe.make_cfg(wl)
-    ws = moe.alloc_workspace(cfg, device=dev)
-    aux = moe.alloc_aux(cfg, device=dev)
-    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16 if wl.act_dtype == 1 else torch.float32,
-                      device=dev)
-    stream = torch.cuda.current_stream()
     # expert weights in the layout the library reads (a one-time load step,
-    # outside the timed region)
-    # (the row-major originals stay for the oracle's CPU baseline)
-    weights = moe.prepare_weights(cfg, {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")})
+    # outside the timed region); the row-major originals stay for the
+    # oracle's CPU baseline
+    weights = moe.prepare_weights(moe.make_cfg(wl),
+                                  {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")})
     torch.cuda.synchronize()
 
-    def step(events=None):
-        moe.moe_layer_forward(cfg, weights, inp["x"], inp["bias"], out, aux, ws,
-                              stage_events=events, stream=stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    hev = HipEvents()
-    ns = moe.N_STAGES + 1
-    evs = hev.create(args.steps * ns)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i * ns:(i + 1) * ns])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stage_ms = [0.0] * moe.N_STAGES
-    for i in range(args.steps):
-        base = i * ns
-        for s in range(moe.N_STAGES):
-            stage_ms[s] += hev.elapsed_ms(evs[base + s], evs[base + s + 1]) / args.steps
-    hev.destroy(evs)
-    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    kept = int(aux["offsets"][-1].item())
-    touched = int((aux["counts"] > 0).sum().item())
+    sampler = ClockSampler()
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    m = time_layer(moe, torch, wl, inp, weights, args.steps, args.warmup, sampler)
+    clocks = sampler.summary()
+    ms_per_step = m["ms_per_step"]
+    print(f"[bench] {ms_per_step:.3f} ms per step", file=sys.stderr, flush=True)
+    kept, touched, st = m["kept"], m["touched"], m["stage_ms"]
     work = algorithmic_work(wl, kept)
     tok_s = wl.T / (ms_per_step / 1e3)
-    st = dict(zip(moe.STAGES, stage_ms))
 
     gate_up_ms = st["ffn_gate_up"]
     achieved_tflops = work["gate_up_flop"] / (gate_up_ms / 1e3) / 1e12
-    kernel_src = os.path.join(ROOT, "routing_expert_ffn_sigmoid_amd", "csrc", "grouped_ffn.hip")
-    traffic = load_traffic(kernel_src, args.workload)
+    traffic = load_traffic(args.workload)
     # algorithmic bytes of the gate/up launch: the touched experts' gate/up
     # weights, the shared expert's, x once, h written once
     es = 2 if wl.act_dtype == 1 else 4
@@ -373,9 +553,10 @@ def main():
                      "kernel": "ffn gate/up grouped GEMM (SwiGLU, routed + shared)",
                      "per_launch_flop": work["gate_up_flop"], "per_launch_bytes": gate_up_bytes,
                      "flop_per_byte": round(intensity, 1), "avg_launch_ms": round(gate_up_ms, 4),
+                     "code_object": code_object_digest(GATE_UP_KERNEL),
                      "beside": secondary})
     layer_tflops = work["layer_flop"] / (ms_per_step / 1e3) / 1e12
-    touched_bytes = touched * 3 * wl.I * wl.H * 2 + 3 * wl.n_shared * wl.I_shared * wl.H * 2
+    tb = touched_weight_bytes(wl, touched)
 
     res = {
         "metric": "MoE-layer tokens/s (route+dispatch+FFN+combine); % MFMA or HBM peak",
@@ -388,17 +569,51 @@ def main():
                    "expert_intermediate": wl.I, "shared": f"{wl.n_shared}x{wl.I_shared}",
                    "capacity": wl.capacity, "parallelism": "single GPU"},
         "roofline": roofline,
-        "layer": {"mfma_frac": round(layer_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                  "tflops": round(layer_tflops, 2), "kept_rows": kept,
-                  "touched_experts": touched,
-                  "touched_weight_gbs": round(touched_bytes / (ms_per_step / 1e3) / 1e9, 1),
-                  "hbm_frac_touched_weights": round(touched_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer": {"roof": "mfma", "mfma_frac": round(layer_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "tflops": round(layer_tflops, 2), "layer_flop": work["layer_flop"],
+                  "step_ms": m["step_ms"], "kept_rows": kept, "touched_experts": touched,
+                  "hbm_frac_touched_weights": round(tb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "stage_ms": {k: round(v, 4) for k, v in st.items()}},
+        "clocks": clocks,
     }
+    if wl.name == workloads.V3_PREFILL.name and not args.no_extra:
+        # the decode and skew configurations of the same layer, same weights,
+        # same process
+        extra = {}
+        for name, sub in (("decode", workloads.V3_DECODE), ("skew", workloads.V3_SKEW)):
+            si = dict(inp)
+            si["x"] = synth.normal((sub.T, sub.H), sub.x_std, torch.bfloat16, dev, sub.seed,
+                                   f"x_T{sub.T}")
+            if sub.bias_kind == "zipf":
+                si["bias"] = synth.zipf_bias(sub.N, sub.bias_param, dev, sub.seed)
+            print(f"[bench] {name}: {sub.name}", file=sys.stderr, flush=True)
+            smp = ClockSampler()
+            r = time_layer(moe, torch, sub, si, weights, args.steps, args.warmup, smp)
+            tbs = touched_weight_bytes(sub, r["touched"])
+            wk = algorithmic_work(sub, r["kept"])
+            e = {"workload": sub.name, "ms_per_step": round(r["ms_per_step"], 4),
+                 "step_ms": r["step_ms"], "tokens_per_s": round(sub.T / (r["ms_per_step"] / 1e3), 1),
+                 "kept_rows": r["kept"], "touched_experts": r["touched"],
+                 "touched_weight_bytes": tbs,
+                 "hbm_frac_touched_weights": round(tbs / (r["step_ms"]["median"] / 1e3) / 1e9
+                                                   / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(wk["layer_flop"] / (r["step_ms"]["median"] / 1e3) / 1e12
+                                    / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+                 "clocks": smp.summary()}
+            if sub.capacity:
+                e["dropped_assignments"], e["tokens_all_dropped"] = r["n_dropped"]
+                e["capacity"] = sub.capacity
+            extra[name] = e
+            del si, r
+            torch.cuda.empty_cache()
+        res.update(extra)
+    res["wave_placement"] = wave_placement(moe, torch)
+    res["environment"] = environment(torch)
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample} tokens", file=sys.stderr,
               flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, inp, aux["logits"], args.cpu_sample)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
 
 

@@ -341,6 +341,15 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* weights,
                              const moe_aux* aux, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Diagnostic (a property of the hardware, not a step of the method): the
+ * SIMD each wave of a large-tile-shaped workgroup (512 threads, one per CU)
+ * runs on.  simd [n_workgroups*8] i32 DEVICE receives, for wave w of
+ * workgroup g, its SIMD number 0..3 at simd[8g + w].  The prefill GEMM
+ * kernels run fastest when waves w and w + 4 share a SIMD (their results do
+ * not depend on it).  n_workgroups < 0, or simd NULL with n_workgroups > 0:
+ * MOE_ERR_INVALID_ARG. */
+moe_status moe_probe_wave_simd(int32_t n_workgroups, int32_t* simd, void* stream);
+
 /* Static string for a status code. */
 const char* moe_status_string(moe_status s);
 

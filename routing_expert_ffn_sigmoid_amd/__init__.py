@@ -29,7 +29,7 @@ EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_load_stats",
            "moe_seq_load_stats", "moe_seq_load_stats_workspace_size", "moe_group_load_stats",
            "moe_pack_weights",
-           "moe_bias_update", "moe_layer_forward", "moe_status_string"]
+           "moe_bias_update", "moe_layer_forward", "moe_status_string", "moe_probe_wave_simd"]
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -105,6 +105,8 @@ def lib():
         L.moe_layer_forward.restype = st
         L.moe_layer_forward.argtypes = [cfgp, ctypes.POINTER(MoeWeights), _vp, _vp, _vp,
                                         ctypes.POINTER(MoeAux), _vp, ctypes.c_size_t, _vp]
+        L.moe_probe_wave_simd.restype = st
+        L.moe_probe_wave_simd.argtypes = [_i32, _vp, _vp]
         _LIB = L
     return _LIB
 
@@ -330,6 +332,15 @@ def moe_bias_update(cfg: MoeCfg, counts, bias, u: float, stream=None):
     code = lib().moe_bias_update(ctypes.byref(cfg), _ptr(counts, torch.int32, "counts", (cfg.N,)),
                                  _ptr(bias, torch.float32, "bias", (cfg.N,)), u, _stream(stream))
     _check(code, "moe_bias_update")
+
+
+def moe_probe_wave_simd(n_workgroups: int, simd, stream=None):
+    """simd: int32 tensor [n_workgroups, 8] on the GPU; receives the SIMD of
+    each wave of large-tile-shaped workgroups."""
+    torch = _torch()
+    code = lib().moe_probe_wave_simd(n_workgroups, _ptr(simd, torch.int32, "simd",
+                                                        (n_workgroups, 8)), _stream(stream))
+    _check(code, "moe_probe_wave_simd")
 
 
 AUX_FIELDS = {"logits": "f32", "topk_idx": "i32", "topk_gate": "f32", "topk_score": "f32",

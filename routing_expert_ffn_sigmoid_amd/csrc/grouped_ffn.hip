@@ -1070,6 +1070,30 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   }
 }
 
+// Wave placement of a large-tile workgroup: wave w of workgroup g reads the
+// number of the SIMD it runs on (bits 5:4 of the HW_ID hardware register)
+// and the workgroup's first wave writes all eight to simd[8g .. 8g + 7].
+// The ping-pong schedule's speed relies on waves w and w + 4 sharing a SIMD
+// (its correctness does not: barriers order every access).  Same launch
+// shape and LDS footprint as ffn_pp_kernel, so one workgroup per CU.
+constexpr int kPPLdsInts = (2 * kPPRows * 2 * kBK4 + kStages * kBuf4Elems) / 2;
+__global__ __launch_bounds__(kBigThreads, 1) void wave_simd_kernel(int32_t* __restrict__ simd) {
+  __shared__ int32_t ids[kPPLdsInts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);  // HW_REG_HW_ID
+  constexpr int kStride = kPPLdsInts / 8;
+  if (lane == 0) ids[wave * kStride] = static_cast<int32_t>((hw_id >> 4) & 3);
+  __syncthreads();
+  if (wave == 0 && lane < 8) simd[blockIdx.x * 8 + lane] = ids[lane * kStride];
+}
+
+hipError_t launch_wave_simd_probe(int32_t* simd, int n_workgroups, hipStream_t st) {
+  if (n_workgroups <= 0) return hipSuccess;
+  wave_simd_kernel<<<n_workgroups, kBigThreads, 0, st>>>(simd);
+  return hipGetLastError();
+}
+
 static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st);
 
 static int device_cus() {

@@ -464,4 +464,9 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
   return MOE_OK;
 }
 
+moe_status moe_probe_wave_simd(int32_t n_workgroups, int32_t* simd, void* stream) {
+  if (n_workgroups < 0 || (n_workgroups > 0 && !simd)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_wave_simd_probe(simd, n_workgroups, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

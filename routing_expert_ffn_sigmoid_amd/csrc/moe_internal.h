@@ -237,6 +237,8 @@ struct FfnGroup {
 hipError_t launch_ffn_bf16(const FfnGroup* groups, int ngroups, int phase, int rows_hint,
                            hipStream_t st);
 hipError_t launch_ffn_f32(const FfnGroup& g, int phase, int max_rows, hipStream_t st);
+// SIMD of each wave of n_workgroups large-tile-shaped workgroups: simd[8g + w]
+hipError_t launch_wave_simd_probe(int32_t* simd, int n_workgroups, hipStream_t st);
 
 hipError_t launch_combine(const void* y_perm, const int32_t* inv_row, const float* gate,
                           const void* y_shared, void* out, int T, int H, int k,
