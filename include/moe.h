@@ -57,7 +57,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size or inconsistent cfg */
   MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
   MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
-  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+  MOE_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+  MOE_ERR_TOO_LARGE = 5    /* moe_layer_forward_noalloc: needs more than the
+                              fixed scratch (MOE_NOALLOC_SCRATCH_BYTES) */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -340,6 +342,26 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* weights,
                              const void* x, const float* bias, void* out,
                              const moe_aux* aux, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * moe_layer_forward without a workspace argument.  Its scratch is one fixed
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends; the call itself allocates nothing.
+ * Arguments, outputs and errors as moe_layer_forward, plus
+ * MOE_ERR_TOO_LARGE when moe_workspace_size(cfg) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a V3-shaped layer up to about
+ * 250 tokens, hidden 2048 / 64 experts up to about 1200), checked before
+ * anything is enqueued.  The first call on a GPU looks up the array's device
+ * address with that GPU current (make it outside any graph capture).  Every
+ * call on one GPU uses the same scratch: calls that overlap in time on one
+ * GPU (other streams, other host threads) race and give undefined results;
+ * calls in stream order are safe, since each call clears what it
+ * accumulates into. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_weights* weights,
+                                     const void* x, const float* bias, void* out,
+                                     const moe_aux* aux, void* stream);
 
 /* Diagnostic (a property of the hardware, not a step of the method): the
  * SIMD each wave of a large-tile-shaped workgroup (512 threads, one per CU)

@@ -19,7 +19,9 @@ from .workloads import BF16, F32, SIGMOID, SOFTMAX, Workload
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_TOO_LARGE) = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 STAGES = ["router_gemm", "route", "dispatch", "ffn_gate_up", "ffn_down", "combine", "stats"]
@@ -29,7 +31,8 @@ EXPORTS = ["moe_workspace_size", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_grouped_ffn_workspace_size", "moe_combine", "moe_load_stats",
            "moe_seq_load_stats", "moe_seq_load_stats_workspace_size", "moe_group_load_stats",
            "moe_pack_weights",
-           "moe_bias_update", "moe_layer_forward", "moe_status_string", "moe_probe_wave_simd"]
+           "moe_bias_update", "moe_layer_forward", "moe_status_string", "moe_probe_wave_simd",
+           "moe_layer_forward_noalloc"]
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -105,6 +108,9 @@ def lib():
         L.moe_layer_forward.restype = st
         L.moe_layer_forward.argtypes = [cfgp, ctypes.POINTER(MoeWeights), _vp, _vp, _vp,
                                         ctypes.POINTER(MoeAux), _vp, ctypes.c_size_t, _vp]
+        L.moe_layer_forward_noalloc.restype = st
+        L.moe_layer_forward_noalloc.argtypes = [cfgp, ctypes.POINTER(MoeWeights), _vp, _vp, _vp,
+                                                ctypes.POINTER(MoeAux), _vp]
         L.moe_probe_wave_simd.restype = st
         L.moe_probe_wave_simd.argtypes = [_i32, _vp, _vp]
         _LIB = L
@@ -362,11 +368,7 @@ def alloc_aux(cfg: MoeCfg, device="cuda") -> dict:
                            device=device) for n, d in AUX_FIELDS.items()}
 
 
-def moe_layer_forward(cfg: MoeCfg, weights: dict, x, bias, out, aux: dict | None, ws,
-                      stage_events=None, stream=None):
-    """weights: dict with w_router, w13, w2, ws13, ws2 (tensors or None).
-    aux: dict of optional output tensors (see alloc_aux).  stage_events:
-    optional list of N_STAGES+1 raw hipEvent_t handles (ints)."""
+def _layer_args(cfg: MoeCfg, weights: dict, x, bias, out, aux: dict | None, stage_events):
     torch = _torch()
     T, N, k, H, I = cfg.T, cfg.N, cfg.k, cfg.H, cfg.I
     wdt = _tdtype(cfg.w_dtype)
@@ -390,9 +392,32 @@ def moe_layer_forward(cfg: MoeCfg, weights: dict, x, bias, out, aux: dict | None
             raise ValueError(f"stage_events needs {N_STAGES + 1} events")
         ev_arr = (_vp * (N_STAGES + 1))(*stage_events)
         a.stage_events = ctypes.cast(ev_arr, ctypes.POINTER(_vp))
+    xp = _ptr(x, _tdtype(cfg.act_dtype), "x", (T, H))
+    bp = _ptr(bias, torch.float32, "bias", (N,))
+    op = _ptr(out, _tdtype(cfg.act_dtype), "out", (T, H))
+    return w, a, ev_arr, xp, bp, op
+
+
+def moe_layer_forward(cfg: MoeCfg, weights: dict, x, bias, out, aux: dict | None, ws,
+                      stage_events=None, stream=None):
+    """weights: dict with w_router, w13, w2, ws13, ws2 (tensors or None).
+    aux: dict of optional output tensors (see alloc_aux).  stage_events:
+    optional list of N_STAGES+1 raw hipEvent_t handles (ints)."""
+    w, a, ev_arr, xp, bp, op = _layer_args(cfg, weights, x, bias, out, aux, stage_events)
     wsp, wsb = _ws(ws)
-    code = lib().moe_layer_forward(
-        ctypes.byref(cfg), ctypes.byref(w), _ptr(x, _tdtype(cfg.act_dtype), "x", (T, H)),
-        _ptr(bias, torch.float32, "bias", (N,)), _ptr(out, _tdtype(cfg.act_dtype), "out", (T, H)),
-        ctypes.byref(a), wsp, wsb, _stream(stream))
+    code = lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(w), xp, bp, op,
+                                   ctypes.byref(a), wsp, wsb, _stream(stream))
+    del ev_arr
     _check(code, "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(cfg: MoeCfg, weights: dict, x, bias, out, aux: dict | None,
+                              stage_events=None, stream=None):
+    """moe_layer_forward on the library's fixed per-GPU scratch (no workspace
+    argument, nothing allocated); MoeError(MOE_ERR_TOO_LARGE) beyond
+    NOALLOC_SCRATCH_BYTES of workspace."""
+    w, a, ev_arr, xp, bp, op = _layer_args(cfg, weights, x, bias, out, aux, stage_events)
+    code = lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), xp, bp, op,
+                                           ctypes.byref(a), _stream(stream))
+    del ev_arr
+    _check(code, "moe_layer_forward_noalloc")

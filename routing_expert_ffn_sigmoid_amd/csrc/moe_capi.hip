@@ -2,9 +2,19 @@
 // layout and the launch sequence of one DeepSeekMoE layer forward.
 #include <limits.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
+
+// Fixed device scratch of moe_layer_forward_noalloc (for callers that cannot
+// allocate).  Every GPU the library runs on holds its own copy of this array
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address (one per GPU) comes from
+// hipGetSymbolAddress, and only that address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -119,6 +129,18 @@ uint32_t bound32(long long rows, long long cols, size_t es) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Arguments of a layer forward other than the workspace.
+moe_status check_layer_args(const moe_cfg* cfg, const moe_weights* w, const void* x,
+                            const void* out) {
+  moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!x || !out || !w->w_router)) return MOE_ERR_INVALID_ARG;
+  if (cfg->k > 0 && (!w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!w->ws13 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 #define MOE_TRY(expr)                                   \
   do {                                                  \
     hipError_t e_ = (expr);                             \
@@ -202,6 +224,9 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration outside the implemented kernels";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the call needs more than the library's fixed scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "unknown moe_status";
 }
@@ -396,12 +421,8 @@ moe_status moe_bias_update(const moe_cfg* cfg, const int32_t* counts, float* bia
 moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const void* x,
                              const float* bias, void* out, const moe_aux* aux, void* ws,
                              size_t ws_bytes, void* stream) {
-  moe_status s = check_cfg(cfg);
+  moe_status s = check_layer_args(cfg, w, x, out);
   if (s != MOE_OK) return s;
-  if (!w) return MOE_ERR_INVALID_ARG;
-  if (cfg->T > 0 && (!x || !out || !w->w_router)) return MOE_ERR_INVALID_ARG;
-  if (cfg->k > 0 && (!w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
-  if (cfg->n_shared > 0 && (!w->ws13 || !w->ws2)) return MOE_ERR_INVALID_ARG;
   const LayerLayout L = layout(cfg);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -462,6 +483,49 @@ moe_status moe_layer_forward(const moe_cfg* cfg, const moe_weights* w, const voi
                        at<char>(ws, L.stats), st));
   MOE_TRY(record(aux, MOE_N_STAGES, st));
   return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current (the first no-alloc call on it).
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 256;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_weights* weights,
+                                     const void* x, const float* bias, void* out,
+                                     const moe_aux* aux, void* stream) {
+  moe_status s = check_layer_args(cfg, weights, x, out);
+  if (s != MOE_OK) return s;
+  if (layout(cfg).total > kNoAllocScratchBytes) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != MOE_OK) return s;
+  // the same launch sequence as moe_layer_forward, on the fixed scratch; it
+  // clears every buffer it accumulates into with a kernel, so what a
+  // previous call left in the scratch does not matter
+  return moe_layer_forward(cfg, weights, x, bias, out, aux, ws, kNoAllocScratchBytes, stream);
 }
 
 moe_status moe_probe_wave_simd(int32_t n_workgroups, int32_t* simd, void* stream) {

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert moe.status_string(code).startswith("MOE_")
 
 
@@ -156,3 +156,28 @@ def test_pack_weights_argument_checks():
     assert L.moe_pack_weights(3, 32, 64, moe.MOE_BF16, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
     # nothing to do
     assert L.moe_pack_weights(0, 32, 64, moe.MOE_BF16, None, None, None) == moe.MOE_OK
+
+
+@needs_lib
+def test_noalloc_forward_rejects_on_the_host():
+    """moe_layer_forward_noalloc checks its arguments and the fixed scratch
+    limit before it touches a device: invalid configurations and missing
+    pointers as moe_layer_forward, MOE_ERR_TOO_LARGE beyond the scratch."""
+    L = moe.lib()
+    w = moe.MoeWeights()
+    for override, code in (({"N": 0}, moe.MOE_ERR_INVALID_ARG), ({"H": 100}, moe.MOE_ERR_UNSUPPORTED)):
+        cfg = moe.make_cfg(workloads.TINY, **override)
+        assert L.moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), None, None, None,
+                                           None, None) == code
+    cfg = moe.make_cfg(workloads.TINY)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(w), None, None, None,
+                                       None, None) == moe.MOE_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)
+    wf = moe.MoeWeights(fake, fake, fake, fake, fake)
+    for wl in (workloads.V3_PREFILL, workloads.V3_DECODE.with_(T=512), workloads.V1):
+        c = moe.make_cfg(wl)
+        assert _ws_size(c)[1] > moe.NOALLOC_SCRATCH_BYTES
+        assert L.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(wf), fake, None, fake,
+                                           None, None) == moe.MOE_ERR_TOO_LARGE
+    # the decode-sized V3 layer fits
+    assert _ws_size(moe.make_cfg(workloads.V3_DECODE))[1] <= moe.NOALLOC_SCRATCH_BYTES
