@@ -241,26 +241,62 @@ def _csv_rows(path_glob):
     return rows
 
 
-def summarize_profile(d: str, workload: str, commands: dict):
+def summarize_profile(d: str, workload: str, commands: dict, steps: int):
     """Turn the raw rocprofv3 output under d (trace/, fetch/, write/,
     copy_fetch/, copy_write/) into profiles/<kernel>_<workload>.txt and the
     gate/up traffic record profiles/ffn_gate_up_traffic_<workload>.json."""
     stats = _csv_rows(os.path.join(d, "trace", "**", "*kernel_stats.csv"))
-    lines = [f"# rocprofv3 summary: DeepSeekMoE layer forward, workload {workload}", ""]
+    trace = _csv_rows(os.path.join(d, "trace", "**", "*kernel_trace.csv"))
+    lines = [f"# rocprofv3 summary: DeepSeekMoE layer forward, workload {workload}", "",
+             f"library code object (gfx950) holding the gate/up kernel: "
+             f"{code_object_digest(GATE_UP_KERNEL)}"]
     for key in ("trace", "fetch", "write", "copy_fetch", "copy_write"):
         if key in commands:
             lines.append(f"{key}: {commands[key]}")
-    lines += ["", "## kernel trace (--kernel-trace --stats), library kernels",
+    lines += ["", "## kernel trace (--kernel-trace --stats), library kernels, all calls",
               f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
-    avg = {}
     for r in stats:
         name = r["Name"]
         if "moe::" not in name:
             continue
         short = name.replace("void ", "").split("(")[0]
-        avg[short] = float(r["AverageNs"]) / 1e3
         lines.append(f"{short:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.1f} "
                      f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f}")
+    # the timed steps only: the last `steps` dispatches of each kernel
+    per = {}
+    for r in trace:
+        name = r["Kernel_Name"]
+        if "moe::" not in name:
+            continue
+        short = name.replace("void ", "").split("(")[0]
+        per.setdefault(short, []).append(
+            (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    # the bench line printed by the traced run itself (its HIP-event stage
+    # times, taken on the same dispatches as the trace)
+    line = None
+    for f in sorted(__import__("glob").glob(os.path.join(d, "trace", "*.out"))):
+        with open(f) as fh:
+            for ln in fh:
+                if ln.startswith('{"metric"'):
+                    line = json.loads(ln)
+    avg = {}
+    lines += ["", f"## the last {steps} calls of each kernel (the timed steps)",
+              f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s}"]
+    for k in sorted(per, key=lambda n: -sum(t for _, t in per[n])):
+        v = [t for _, t in sorted(per[k])][-steps:]
+        vs = sorted(v)
+        avg[k] = sum(v) / len(v)
+        lines.append(f"{k:60s} {len(v):6d} {avg[k]:10.1f} {vs[len(vs) // 2]:10.1f} {vs[0]:10.1f}")
+    if line is not None:
+        ev = line["layer"]["stage_ms"]
+        lines += ["", "## the traced run's own bench line (HIP events on the launch stream, same steps)",
+                  f"ms_per_step {line['ms_per_step']}; stage averages (ms): " +
+                  ", ".join(f"{k} {v}" for k, v in ev.items())]
+        gu = [k for k in avg if "ffn" in k and "<" in k and "true" in k[k.find("<"):]]
+        if gu:
+            k = max(gu, key=lambda n: avg[n])
+            lines.append(f"gate/up: trace {avg[k] / 1e3:.4f} ms vs events {ev['ffn_gate_up']:.4f} ms "
+                         f"({100 * (ev['ffn_gate_up'] / (avg[k] / 1e3) - 1):+.2f} %)")
 
     def per_kernel(sub, counter):
         acc = {}
@@ -485,14 +521,15 @@ def main():
         return
     if args.summarize_profile:
         cmd = "rocprofv3 {opt} -d <dir> -o run --output-format csv -- python3 bench.py {args}"
-        run = f"--workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-extra"
+        run = f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} " \
+              f"--no-cpu-baseline --no-extra"
         pmc = f"--workload {args.workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extra"
         commands = {"trace": cmd.format(opt="--kernel-trace --stats", args=run),
                     "fetch": cmd.format(opt="--pmc FETCH_SIZE", args=pmc),
                     "write": cmd.format(opt="--pmc WRITE_SIZE", args=pmc),
                     "copy_fetch": cmd.format(opt="--pmc FETCH_SIZE", args="--calibrate-copy"),
                     "copy_write": cmd.format(opt="--pmc WRITE_SIZE", args="--calibrate-copy")}
-        summarize_profile(args.summarize_profile, args.workload, commands)
+        summarize_profile(args.summarize_profile, args.workload, commands, args.steps)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the layer on a single MI355X "
