@@ -400,14 +400,26 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   const int e0 = lane * 4;
   const bool valid = e0 < N;  // N is a multiple of 4
 
+  // logits: the K-split partials added in split order (0 + p0) + p1 + ...;
+  // the partials of up to 8 splits are loaded before any is added, so their
+  // memory latencies overlap
   float l[4] = {0.f, 0.f, 0.f, 0.f};
   if (valid) {
-    for (int s = 0; s < p.splits; ++s) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p.part + (static_cast<int64_t>(s) * p.T + t) * N + e0);
-      l[0] += v.x;
-      l[1] += v.y;
-      l[2] += v.z;
-      l[3] += v.w;
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part + static_cast<int64_t>(t) * N + e0);
+    const int64_t sstride = static_cast<int64_t>(p.T) * N / 4;  // f32x4 per split
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < p.splits) v[u] = src[(s0 + u) * sstride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < p.splits) {
+          l[0] += v[u].x;
+          l[1] += v[u].y;
+          l[2] += v[u].z;
+          l[3] += v[u].w;
+        }
     }
     *reinterpret_cast<f32x4*>(p.logits + static_cast<int64_t>(t) * N + e0) =
         f32x4{l[0], l[1], l[2], l[3]};
