@@ -65,3 +65,19 @@ def test_code_object_digest_of_the_built_library():
     r = bench.code_object_digest("route_kernel")
     assert r is not None and r != d
     assert bench.code_object_digest("no_such_kernel_name") is None
+
+
+def test_row_rel_l2_flags_one_bad_row_and_nonzero_zero_rows():
+    from gpu_common import normwise, row_rel_l2
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal((4096, 64))
+    got = ref * (1 + 1e-3 * rng.standard_normal(ref.shape))
+    got[17] *= 1.05                       # one row 5 % off
+    assert normwise(got, ref)[1] < 5e-3   # the block norm does not see it
+    rows = row_rel_l2(got, ref)
+    assert int(np.argmax(rows)) == 17 and rows[17] > 4e-2
+    ref[5] = 0.0
+    got[5] = 0.0
+    assert row_rel_l2(got, ref)[5] == 0.0
+    got[5, 3] = 1e-30
+    assert np.isinf(row_rel_l2(got, ref)[5])
