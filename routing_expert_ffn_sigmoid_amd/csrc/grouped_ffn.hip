@@ -33,6 +33,8 @@
 //    tile list out in rounds (each XCD a run of consecutive tiles per round),
 //    which keeps the XCDs equally loaded; the small-segment kernel gives each
 //    XCD a contiguous eighth of the list.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "lds_dma.h"
 
@@ -68,6 +70,33 @@ __device__ __forceinline__ int seg_end(const FfnGroup& g, int s) {
   return g.seg_off ? g.seg_off[s + 1] : g.rows;
 }
 
+// Group `grp` of a launch as a value chosen field by field: no address into
+// the kernel arguments is formed, so they are not copied to private memory
+// (whose loads would count among the loads in flight).
+__device__ __forceinline__ FfnGroup pick_group(const FfnLaunch& a, int grp) {
+  const bool o = grp != 0;
+  const FfnGroup& g0 = a.g[0];
+  const FfnGroup& g1 = a.g[1];
+  FfnGroup g;
+  g.A = o ? g1.A : g0.A;
+  g.lda = o ? g1.lda : g0.lda;
+  g.row_index = o ? g1.row_index : g0.row_index;
+  g.seg_off = o ? g1.seg_off : g0.seg_off;
+  g.nseg = o ? g1.nseg : g0.nseg;
+  g.rows = o ? g1.rows : g0.rows;
+  g.W = o ? g1.W : g0.W;
+  g.w_stride = o ? g1.w_stride : g0.w_stride;
+  g.Out = o ? g1.Out : g0.Out;
+  g.ldo = o ? g1.ldo : g0.ldo;
+  g.K = o ? g1.K : g0.K;
+  g.n_out = o ? g1.n_out : g0.n_out;
+  g.up_off = o ? g1.up_off : g0.up_off;
+  g.a_bytes = o ? g1.a_bytes : g0.a_bytes;
+  g.w_bytes = o ? g1.w_bytes : g0.w_bytes;
+  g.o_bytes = o ? g1.o_bytes : g0.o_bytes;
+  return g;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Threads beyond the first 256 of a larger workgroup pass the same barriers
@@ -83,7 +112,8 @@ __device__ __forceinline__ void build_tile_starts_idle() {
 
 // Exclusive prefix of `cnt` tiles per flat segment into tstart[0..n].
 template <int BM>
-__device__ void build_tile_starts(const FfnLaunch& a, int nsegT, int* tstart, int* tmp) {
+__device__ __forceinline__ void build_tile_starts(const FfnLaunch& a, int nsegT, int* tstart,
+                                                  int* tmp) {
   const int tid = threadIdx.x;
   // each thread owns 4 consecutive segments
   int local[4];
@@ -94,7 +124,7 @@ __device__ void build_tile_starts(const FfnLaunch& a, int nsegT, int* tstart, in
     int c = 0;
     if (i < nsegT) {
       const int grp = (a.ngroups > 1 && i >= a.g[0].nseg) ? 1 : 0;
-      const FfnGroup& g = grp ? a.g[1] : a.g[0];
+      const FfnGroup g = pick_group(a, grp);
       const int s = grp ? i - a.g[0].nseg : i;
       const int rows = seg_end(g, s) - seg_begin(g, s);
       c = ((rows + BM - 1) / BM) * (grp ? a.nt[1] : a.nt[0]);
@@ -429,42 +459,78 @@ __device__ __forceinline__ void big_compute(const bf16_t* __restrict__ Ab,
   }
 }
 
+// v (in a vector register) as a value the compiler cannot see through, so
+// that a constant used once is materialised where it is used instead of
+// being held in a register across the kernel's loops
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// An LDS buffer's address as a value the compiler cannot trace back to the
+// buffer.  The ping-pong kernel orders its direct global->LDS loads and the
+// LDS reads of the same buffers with its own counted waits and barriers; on
+// addresses it can trace, the compiler adds waits of its own before the
+// reads, counted for the most cautious path through the kernel's loops,
+// which hold back loads and stores the reads do not depend on.
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+template <typename T>
+__device__ __forceinline__ T* lds_opaque(T* p) {
+  __attribute__((address_space(3))) T* q = (__attribute__((address_space(3))) T*)p;
+  asm volatile("" : "+s"(q));
+  return (T*)q;
+}
+
 // SwiGLU of a gate/up accumulator pair, rounded to bf16 and packed: two h
-// columns per 32-bit word (lower column in the low half)
+// columns per 32-bit word (lower column in the low half).  silu(g) =
+// g * 1/(1 + e^-g) with the hardware reciprocal (1 ulp), far below the bf16
+// rounding of h; e^-g = inf gives 1/inf = 0, so silu -> -0 as g -> -inf.
 __device__ __forceinline__ uint32_t swiglu_pack(float g0, float g1, float u0, float u1) {
-  const float h0 = g0 / (1.0f + __expf(-g0)) * u0;
-  const float h1 = g1 / (1.0f + __expf(-g1)) * u1;
+  const float h0 = g0 * __builtin_amdgcn_rcpf(1.0f + __expf(-g0)) * u0;
+  const float h1 = g1 * __builtin_amdgcn_rcpf(1.0f + __expf(-g1)) * u1;
   return pack_bf16x2(h0, h1);
 }
 
+// Stores a tile epilogue issues per wave, whatever the tile's height: the
+// count the next tile's first wait is built from.
+constexpr int kPPStores = 16;
+
 // Gate/up tile epilogue straight from registers: per M-block and lane, h of
 // 4 consecutive columns of one row (8 bytes) for each of the wave's two
-// 16-column blocks; rows past mv and columns past n_out are not stored.
+// 16-column blocks.  Every store is issued (a lane whose row lies past mv or
+// whose columns lie past n_out gets an offset past the buffer's bound, which
+// the hardware drops), and a short tile pads with dropped stores, so a wave
+// issues exactly kPPStores store instructions.  The buffer bound (o_bytes)
+// is at most 0xFFFFFF00, so a dropped offset never wraps.
 template <int NJ>
-__device__ __forceinline__ void gate_up_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
-                                                 int nmbw, int wm, int wn, int nt, int mrow0,
-                                                 int mv) {
-  const int lane = threadIdx.x & 63;
-  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+__device__ __forceinline__ int gate_up_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
+                                                int wm, int wn, int nt, int mrow0, int mv) {
+  const int lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;  // derived here
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(g.Out, g.o_bytes);
   const int rl = lane & 15;
   const int cq = (lane >> 4) * 4;
+  const uint32_t ldo2 = static_cast<uint32_t>(g.ldo) * 2u;
+  u32x2 last;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    if (j < nmbw) {
-      const int r = (2 * j + wm) * 16 + rl;
-      if (r < mv) {
-        bf16_t* orow = Out + static_cast<int64_t>(mrow0 + r) * g.ldo;
+    const int r = (2 * j + wm) * 16 + rl;
+    const uint32_t rowoff = static_cast<uint32_t>(mrow0 + r) * ldo2;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = nt * 128 + wn * 32 + nb * 16 + cq;
-          if (col < g.n_out)
-            *reinterpret_cast<u32x2*>(orow + col) =
-                u32x2{swiglu_pack(acc[j][nb][0], acc[j][nb][1], acc[j][nb + 2][0], acc[j][nb + 2][1]),
-                      swiglu_pack(acc[j][nb][2], acc[j][nb][3], acc[j][nb + 2][2], acc[j][nb + 2][3])};
-        }
-      }
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = nt * 128 + wn * 32 + nb * 16 + cq;
+      const uint32_t off =
+          (r < mv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
+      last = u32x2{swiglu_pack(acc[j][nb][0], acc[j][nb][1], acc[j][nb + 2][0], acc[j][nb + 2][1]),
+                   swiglu_pack(acc[j][nb][2], acc[j][nb][3], acc[j][nb + 2][2], acc[j][nb + 2][3])};
+      __builtin_amdgcn_raw_buffer_store_b64(last, ro, off, 0, 0);
     }
   }
+  if constexpr (2 * NJ < kPPStores) {
+    const uint32_t drop = opaque_u32(0xFFFFFFF0u);
+#pragma unroll
+    for (int j = 2 * NJ; j < kPPStores; ++j) __builtin_amdgcn_raw_buffer_store_b64(last, ro, drop, 0, 0);
+  }
+  return kPPStores;
 }
 
 // Down tile epilogue through LDS, so the outputs leave as whole rows.  Pass
@@ -479,55 +545,68 @@ __device__ __forceinline__ void gate_up_epilogue(const FfnGroup& g, const f32x4 
 // free when this is called) alternate, so one barrier per pass orders the
 // writes before the reads, and the reads of pass p before the writes of
 // pass p + 2 (each wave's reads complete before its stores issue, which
-// precede its arrival at the next barrier).  Rows past mv and columns past
-// n_out are not stored (n_out is a multiple of 8).
+// precede its arrival at the next barrier).  Every store is issued (rows
+// past mv and columns past n_out get an offset past the buffer's bound,
+// which the hardware drops), and a short tile pads with dropped stores, so a
+// wave issues exactly kPPStores store instructions.
 template <int NJ>
-__device__ __forceinline__ void staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
-                                                int nmbw, int wm, int wn, int nt, int mrow0,
-                                                int mv, bf16_t* S0, bf16_t* S1) {
+__device__ __forceinline__ int staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
+                                               int wm, int wn, int nt, int mrow0, int mv,
+                                               bf16_t* S0, bf16_t* S1) {
   constexpr int COLS = 256;                 // output columns of a tile
   constexpr int RB = COLS * 2;              // bytes of a staged row
   constexpr int CPR = RB / 16;              // 16-byte chunks per staged row
   constexpr int NI = 32 * RB / 1024;        // 1 KiB pieces per pass
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_uniform(static_cast<int>(threadIdx.x >> 6));
+  // lane values derived here, not kept in registers across the tile
+  const int tid = static_cast<int>(opaque_u32(threadIdx.x));
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
   const int rloc = wm * 16 + (lane & 15);   // staged row of this lane's accumulators
   const int q = lane >> 4;                  // 4-column group inside a 16-column block
-  bf16_t* Out = static_cast<bf16_t*>(g.Out);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(g.Out, g.o_bytes);
+  const uint32_t ldo2 = static_cast<uint32_t>(g.ldo) * 2u;
+  u32x4 last;
 #pragma unroll
   for (int p = 0; p < NJ; ++p) {
-    if (p < nmbw) {  // tile-uniform
-      char* S = reinterpret_cast<char*>(p & 1 ? S1 : S0);
-      char* srow = S + rloc * RB;
+    char* S = reinterpret_cast<char*>(p & 1 ? S1 : S0);
+    char* srow = S + rloc * RB;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = wn * 64 + nb * 16 + q * 4;
-        const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
-        const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
-        *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
-            u32x2{w0, w1};
-      }
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = wn * 64 + nb * 16 + q * 4;
+      const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
+      const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
+      *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
+          u32x2{w0, w1};
+    }
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-      for (int i0 = 0; i0 < NI; i0 += 8) {
-        const int off = (i0 + wave) * 1024 + lane * 16;
-        const int r = off / RB;
-        const int c = (off % RB) >> 4;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(S + r * RB + ((c ^ (r % CPR)) << 4));
-        const int row = 32 * p + r;
-        const int col = nt * COLS + c * 8;
-        if (row < mv && col < g.n_out)
-          *reinterpret_cast<u32x4*>(Out + static_cast<int64_t>(mrow0 + row) * g.ldo + col) = v;
-      }
+    for (int i0 = 0; i0 < NI; i0 += 8) {
+      const int off = (i0 + wave) * 1024 + lane * 16;
+      const int r = off / RB;
+      const int c = (off % RB) >> 4;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(S + r * RB + ((c ^ (r % CPR)) << 4));
+      const int row = 32 * p + r;
+      const int col = nt * COLS + c * 8;
+      const uint32_t o = (row < mv && col < g.n_out)
+                             ? static_cast<uint32_t>(mrow0 + row) * ldo2 + static_cast<uint32_t>(col) * 2u
+                             : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, o, 0, 0);
+      last = v;
     }
   }
+  if constexpr (2 * NJ < kPPStores) {
+    const uint32_t drop = opaque_u32(0xFFFFFFF0u);
+#pragma unroll
+    for (int j = 2 * NJ; j < kPPStores; ++j) __builtin_amdgcn_raw_buffer_store_b128(last, ro, drop, 0, 0);
+  }
+  return kPPStores;
 }
 
-// Tiles run back to back: the first stage of the next tile is loaded during
-// the last step of the current one, before the current tile's stores, so the
-// next tile's first wait skips those stores (vmcnt retires in issue order)
-// and no tile starts with an empty pipeline.
+// In the 2-stage kernel tiles run back to back: the first stage of the next
+// tile is loaded during the last step of the current one, before the
+// current tile's stores, so the next tile's first wait skips those stores
+// (vmcnt retires in issue order) and no tile starts with an empty pipeline.
 // Tile order inside one segment of mtc row tiles x ntc column tiles: row
 // tiles are taken in groups of up to kGroupM, and inside a group the order is
 // column-major (all row tiles of the group for column tile 0, then column 1,
@@ -792,9 +871,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // k-step's fragments from LDS into registers, and issues its part of a
 // later stage's loads, while the other group issues that k-step's MFMAs
 // back to back.  Each SIMD's matrix core is then fed by one wave at a time
-// with no LDS waits between its MFMAs.  Gate/up tiles store h straight from
-// registers, group 0 while group 1 runs the last MFMAs; down tiles (256
-// output columns) go through the staged epilogue.
+// with no LDS waits between its MFMAs.
+// Tiles run back to back in one stream of k-steps: the last three k-steps
+// of a tile load the first stages of the workgroup's next tile into the
+// buffers they have finished with, so a tile starts on stages already in
+// LDS, and gate/up tiles keep the half-step offset of the groups across the
+// tile boundary (group 0 stores its h while group 1 runs the last MFMAs,
+// group 1 while group 0 runs the next tile's first ones).  Down tiles (256
+// output columns) go through the staged epilogue in the activation buffer
+// that the next tile fills last.
 // An activation buffer holds two k-steps as 128-byte rows, so one wave's
 // activation load covers 8 whole 128-byte lines.  (Loading each k-step as
 // 64-byte rows, half of 16 lines per load, measured 6 % slower on both
@@ -810,20 +895,185 @@ constexpr int kBuf4Elems = 256 * kBK4;  // 16 KiB weight stage (256 weight rows)
 // tiles 5 % slower.
 constexpr int kPPRows = 256;
 
-// wait until at most N vector-memory instructions of this wave are
-// outstanding; N < 0: no wait
-template <int N>
-__device__ __forceinline__ void pp_wait_n() {
-  if constexpr (N >= 0) wait_vmcnt<N>();
+// A tile of the ping-pong kernel (wave-uniform values).
+struct PPTile {
+  int grp, s, nt, mrow0, mv, nmbw, nk;
+};
+
+// Tile L of the flat tile list: segment by binary search over the tile
+// starts, rows from the segment table, both in LDS (no memory instruction,
+// so nothing enters the count of loads in flight).
+__device__ __forceinline__ PPTile pp_decode(const FfnLaunch& a, const int* tstart,
+                                            const int* sbeg, const int* srows, int nsegT, int L) {
+  int i0 = 0, i1 = nsegT;
+  while (i1 - i0 > 1) {
+    const int mid = (i0 + i1) >> 1;
+    if (tstart[mid] <= L) i0 = mid;
+    else i1 = mid;
+  }
+  i0 = wave_uniform(i0);
+  PPTile t;
+  t.grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
+  t.s = t.grp ? i0 - a.g[0].nseg : i0;
+  const int r0 = wave_uniform(sbeg[i0]);
+  const int rows = wave_uniform(srows[i0]);
+  const int mtc = (rows + kPPRows - 1) / kPPRows;
+  const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
+  const int local = L - wave_uniform(tstart[i0]);
+  int mt;
+  tile_nm(local, mtc, t.grp ? a.nt[1] : a.nt[0], t.nt, mt);
+  t.mrow0 = r0 + mt * rpt;
+  t.mv = min(rpt, rows - mt * rpt);
+  t.nmbw = (((t.mv + 15) >> 4) + 1) >> 1;  // M-blocks per wave
+  t.nk = (t.grp ? a.g[1].K : a.g[0].K) / kBK4;
+  return t;
 }
 
-// One tile of the ping-pong kernel; the activations of k-steps 2i and
-// 2i + 1 arrive together as 128-byte rows in buffer X0 (i even) or X1
-// (i odd).
+// Where a tile's operands come from.  Activation loads: 8 rows x 128 bytes
+// per wave instruction; row group q = p*8 + wave covers tile rows [8q, 8q+8);
+// lane -> row 8q + lane/8, physical chunk lane%8, logical chunk
+// (lane%8) ^ ((row >> 1) & 7), and (row >> 1) & 7 = 4*(wave & 1) + lane/16
+// for every p.  Rows past the tile's valid ones read from past the buffer's
+// end, which returns zeros without a memory request (their results are
+// never stored; a buffer within 256 MiB of 4 GiB repeats the last valid row
+// instead, so that no offset wraps); groups past the tile's height are not
+// loaded.  Weights, tiled: the wave copies the KiB of k-block `step` of row
+// blocks `wave` and 8 + `wave` (gate/up: the gate and the up block of the
+// same columns) into LDS slots `wave` and 8 + `wave`, in fragment order; a
+// block whose columns lie past n_out (never stored) reads block 0 instead,
+// so every address stays inside the expert's weights.
+struct PPLoads {
+  const void* a_base;
+  const void* w_base;
+  uint32_t a_bytes, w_bytes;
+  uint32_t aoff[4];      // per lane: activation row byte offset + chunk of row group p*8 + wave
+  uint32_t wrow0, wrow1; // uniform: byte offsets of the wave's two weight row blocks
+  int g8;                // row groups of 8 the tile loads
+};
+
+// The row_index entries of this lane's four row groups, as exactly four
+// buffer loads (without a row_index the buffer is empty: they return 0
+// without touching memory), so that the count of loads in flight is known.
+__device__ __forceinline__ void pp_rows_issue(const FfnGroup& g, const PPTile& t, int wave,
+                                              int lane, uint32_t (&raw)[4]) {
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(g.row_index, g.row_index ? 0x7FFFFFF0u : 0u);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = (p * 8 + wave) * 8 + (lane >> 3);
+    const int prow = t.mrow0 + min(row, t.mv - 1);
+    raw[p] = __builtin_amdgcn_raw_buffer_load_b32(rr, static_cast<uint32_t>(prow) * 4u, 0, 0);
+  }
+}
+
+// the weight half of a tile's load state
+// The four row_index entries of every lane of the wave, brought into the
+// wave's 256-byte slot of LDS by one direct load (lane l fetches entry l % 32:
+// row group (l % 32) / 8, row l % 8 of the group, at slot[l]; lanes 32..63
+// repeat lanes 0..31), so no register holds them while the tile's last
+// steps run.
+__device__ __forceinline__ void pp_rows_issue_lds(const FfnGroup& g, const PPTile& t, int wave,
+                                                  int lane, int32_t* slot) {
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(g.row_index, g.row_index ? 0x7FFFFFF0u : 0u);
+  lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;
+  const int l = lane & 31;
+  const int row = ((l >> 3) * 8 + wave) * 8 + (l & 7);
+  const int prow = t.mrow0 + min(row, t.mv - 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)slot, 4,
+                                           static_cast<uint32_t>(prow) * 4u, 0, 0, 0);
+}
+// this lane's four entries from the slot (the load has completed)
+__device__ __forceinline__ void pp_rows_read_lds(const int32_t* slot, int lane,
+                                                 uint32_t (&raw)[4]) {
+  lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) raw[p] = static_cast<uint32_t>(slot[p * 8 + (lane >> 3)]);
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ void pp_wloads(const FfnGroup& g, const PPTile& t, int wave,
+                                          PPLoads& L) {
+  L.w_base = static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(t.s) * g.w_stride;
+  L.w_bytes = g.w_bytes;
+  const uint32_t krow_bytes = static_cast<uint32_t>(g.K) * 2u;
+  const int col0 = (SWIGLU ? t.nt * 128 : t.nt * 256) + wave * 16;
+  const int c0 = col0 < g.n_out ? col0 : 0;
+  const int c1 = SWIGLU ? g.up_off + c0 : (col0 + 128 < g.n_out ? col0 + 128 : 0);
+  L.wrow0 = wave_uniform(static_cast<uint32_t>(c0) * krow_bytes);
+  L.wrow1 = wave_uniform(static_cast<uint32_t>(c1) * krow_bytes);
+}
+// the activation half, from the row_index values pp_rows_issue loaded
+__device__ __forceinline__ void pp_aloads(const FfnGroup& g, const PPTile& t, int wave, int lane,
+                                          const uint32_t (&raw)[4], PPLoads& L) {
+  lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;  // derived here, not held across the tile
+  L.a_base = g.A;
+  L.a_bytes = g.a_bytes;
+  const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const bool zero_pad = g.a_bytes <= 0xF0000000u;
+  const bool gather = g.row_index != nullptr;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = (p * 8 + wave) * 8 + (lane >> 3);
+    const int prow = gather ? static_cast<int>(raw[p]) : t.mrow0 + min(row, t.mv - 1);
+    L.aoff[p] = (row < t.mv || !zero_pad)
+                    ? static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16
+                    : g.a_bytes;
+  }
+  L.g8 = 4 * t.nmbw;
+}
+
+// activations of k-steps step, step + 1 (step even) into buffer Xb: NA
+// loads per wave, row groups p*8 + wave for p < NA; a group past the tile's
+// height reads zeros (its offset lies past the buffer's bound) into rows no
+// M-block of the tile reads, so every wave issues the same count and the
+// waits below are compile-time constants
+template <int NA>
+__device__ __forceinline__ void pp_issue_a(const PPLoads& L, int step, bf16_t* Xb, int wave) {
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(L.a_base, L.a_bytes);
+  const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
+#pragma unroll
+  for (int p = 0; p < NA; ++p)
+    dma16(ra, L.aoff[p], kb, Xb + (p * 8 + wave) * 8 * (2 * kBK4));
+}
+// weights of k-step `step` into stage Bb
+__device__ __forceinline__ void pp_issue_w(const PPLoads& L, int step, bf16_t* Bb, int wave,
+                                           uint32_t lane16) {
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(L.w_base, L.w_bytes);
+  const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
+  dma16(rb, lane16, L.wrow0 + kw, Bb + wave * kTileElems);
+  dma16(rb, lane16, L.wrow1 + kw, Bb + (8 + wave) * kTileElems);
+}
+
+// One tile, its epilogue and the first stages of the workgroup's next tile
+// (Ln < total; without one, the same loads over empty buffers); on return t
+// and cur describe the next tile.
+//
+// Load order of a wave.  Step k of a tile with nk >= 8 steps issues I(k):
+//   k + 3 < nk: A(k+2, k+3) if k is even (NA loads), at k = nk - 4 the
+//               next tile's row_index load R (1), W(k+3) (2);
+//   otherwise:  k = nk-3: W'(0); k = nk-2: A'(0,1) (4 loads), W'(1);
+//               k = nk-1: W'(2)  (the next tile's first stages);
+// and between a tile's last step and the next tile's first the epilogue's
+// kPPStores stores (S).  The first tile of a workgroup starts with W(0),
+// A(0,1), W(1), W(2), the same order, and waits for all but W(2).  Stage j
+// (W(j) and the activation pair holding j) is read by group 0 in phase 2j
+// and by group 1 in phase 2j + 1; before the barrier that ends phase 2j - 1
+// every wave waits for its own loads of stage j: after step j - 1 it lets
+// only the loads issued after the last one stage j needs stay in flight
+// (loads complete in issue order):
+//   even k: |I(k-1)| + |I(k)|         (k = 0: W'(2) + S + |I(0)|)
+//   odd k:  |I(k-1)| - (A count) + |I(k)|     (the pair is first in I(k-1))
+// which is 4 + NA (even) and 4 (odd) in the middle of a tile, 4 + NA + S at
+// k = 0, 4 + NA + 1 at nk-4, 5 at nk-3, 8 at nk-2 and 4 at nk-1; R has
+// landed at the start of step nk-2 once at most W(nk-1) and W'(0) (4) are in
+// flight.  A load into a buffer is issued only after the barrier by which
+// both groups have read that buffer's last stage (W(k+3) goes where W(k-1)
+// was, A(k+2, k+3) where A(k-2, k-1) was).
 template <int NMBW, bool SWIGLU>
-__device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0, int mv,
-                                     bf16_t* X0, bf16_t* X1, bf16_t* B0, bf16_t* B1, bf16_t* B2,
-                                     bf16_t* B3) {
+__device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, const int* sbeg,
+                                        const int* srows, int nsegT, int Ln, int total,
+                                        PPTile& t, PPLoads& cur, bf16_t* X0, bf16_t* X1,
+                                        bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3,
+                                        int32_t* rslot) {
   static_assert(NMBW >= 1 && NMBW <= 8, "tiles hold at most 256 rows");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -831,65 +1081,10 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   const int grp = wave >> 2;
   const int wm = wave & 1;
   const int wn = wave >> 1;
-  const int K = wave_uniform(g.K);
-  const int nk = K / kBK4;  // multiple of 4
-
-  // Activation loads: 8 rows x 128 bytes per wave instruction; row group
-  // q = p*8 + wave covers tile rows [8q, 8q+8); lane -> row 8q + lane/8,
-  // physical chunk lane%8, logical chunk (lane%8) ^ ((row >> 1) & 7), and
-  // (row >> 1) & 7 = 4*(wave & 1) + lane/16 for every p.  Rows past the
-  // tile's valid ones read from past the buffer's end, which returns zeros
-  // without a memory request (their results are never stored; a buffer
-  // within 256 MiB of 4 GiB repeats the last valid row instead, so that no
-  // offset wraps); groups past the tile's height are not loaded.
-  const int logical = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-      static_cast<const bf16_t*>(g.W) + static_cast<int64_t>(s) * g.w_stride, g.w_bytes);
-  constexpr int G8 = 4 * NMBW;  // row groups of 8 the tile loads
-  constexpr int NAG = (G8 + 7) / 8;
-  const bool zero_pad = g.a_bytes <= 0xF0000000u;
-  uint32_t aoff[NAG];
-#pragma unroll
-  for (int p = 0; p < NAG; ++p) {
-    const int row = (p * 8 + wave) * 8 + (lane >> 3);
-    if (row < mv || !zero_pad) {
-      int prow = mrow0 + min(row, mv - 1);
-      if (g.row_index) prow = g.row_index[prow];
-      aoff[p] = static_cast<uint32_t>(prow) * static_cast<uint32_t>(g.lda) * 2u + logical * 16;
-    } else {
-      aoff[p] = g.a_bytes;
-    }
-  }
-  // Weights, tiled: the wave copies the KiB of k-block `step` of row blocks
-  // `wave` and 8 + `wave` (gate/up: the gate and the up block of the same
-  // columns) into LDS slots `wave` and 8 + `wave`, in fragment order.  A
-  // block whose columns lie past n_out (their results are never stored)
-  // reads block 0 instead, so every address stays inside the expert's
-  // weights (the buffer's range check covers the per-lane offset only).
-  const uint32_t krow_bytes = static_cast<uint32_t>(K) * 2u;
-  const int col0 = (SWIGLU ? nt * 128 : nt * 256) + wave * 16;
-  const int c0 = col0 < g.n_out ? col0 : 0;
-  const int c1 = SWIGLU ? g.up_off + c0 : (col0 + 128 < g.n_out ? col0 + 128 : 0);
-  const uint32_t boff0 = static_cast<uint32_t>(c0) * krow_bytes + lane * 16u;
-  const uint32_t boff1 = static_cast<uint32_t>(c1) * krow_bytes + lane * 16u;
-
-  // k-steps step, step + 1 (step even)
-  auto issue_a = [&](int step, bf16_t* Xb) {
-    const uint32_t kb = static_cast<uint32_t>(step) * (kBK4 * 2);
-#pragma unroll
-    for (int p = 0; p < NAG; ++p)
-      if (p * 8 + wave < G8) dma16(ra, aoff[p], kb, Xb + (p * 8 + wave) * 8 * (2 * kBK4));
-  };
-  auto issue_w = [&](int step, bf16_t* Bb) {
-    const uint32_t kw = static_cast<uint32_t>(step) * 1024u;
-    dma16(rb, boff0, kw, Bb + wave * kTileElems);
-    dma16(rb, boff1, kw, Bb + (8 + wave) * kTileElems);
-  };
-  // activation loads of this wave per pair of k-steps: NA0, one more with
-  // `extra`
-  constexpr int NA0 = G8 / 8;
-  const bool extra = wave < (G8 % 8);
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
+  const int nk = wave_uniform(t.nk);  // multiple of 4, at least 8
+  const bool has_next = Ln < total;
+  constexpr int NA = (4 * NMBW + 7) / 8;  // activation loads per wave and pair of steps
 
   // a whole k-step's fragments: M-blocks 2j + wm (j < NMBW), weight blocks
   // of columns 32wn .. 32wn + 31 (gate and up); row 16*block + lane%16 has
@@ -897,7 +1092,7 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
   const int swz = (lane & 15) >> 1;
   const int arow = (wm * 16 + (lane & 15)) * (2 * kBK4);
   bf16x8 af[NMBW], bf[4];
-  auto read = [&](const bf16_t* Xb, int half, const bf16_t* Bb) {
+  auto read = [&](const bf16_t* Xb, int half, const bf16_t* Bb) __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
       bf[nb] = as_bf16x8(
@@ -907,13 +1102,12 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
     for (int j = 0; j < NMBW; ++j)
       af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * (2 * kBK4)));
   };
-
   f32x4 acc[NMBW][4];
 #pragma unroll
   for (int j = 0; j < NMBW; ++j)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&]() {
+  auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NMBW; ++j)
 #pragma unroll
@@ -921,124 +1115,147 @@ __device__ __noinline__ void pp_tile(const FfnGroup& g, int s, int nt, int mrow0
         acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
   };
 
-  // prologue: A(0,1) W0 W1 A(2,3) W2 W3; k-step 0 needs A(0,1) and W0
-  issue_a(0, X0);
-  issue_w(0, B0);
-  issue_w(1, B1);
-  issue_a(2, X1);
-  issue_w(2, B2);
-  issue_w(3, B3);
-  if (extra) wait_vmcnt<6 + NA0 + 1>();
-  else wait_vmcnt<6 + NA0>();
-  __builtin_amdgcn_s_barrier();
-  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
-  __builtin_amdgcn_sched_barrier(0);
-  // k-step k reads stage k in phase 2k (group 0) or 2k + 1 (group 1) and
-  // computes it in the phase after.  At the start of its read phase a wave
-  // issues W(k + 3) into the weight buffer of k - 1 and, for even k, first
-  // A(k + 2, k + 3) into the activation buffer of k - 2 and k - 1; both
-  // groups read k - 1 by phase 2k - 1.  Before the barrier that closes phase
-  // 2k + 1 every wave waits for its own loads of stage k + 1.  Even k:
-  // W(k + 1), then W(k + 2), A(k + 2, k + 3) and W(k + 3) may stay
-  // outstanding.  Odd k: A(k + 1, k + 2) (after W(k + 1)), then W(k + 2) and
-  // W(k + 3) may.  In the last four k-steps nothing is issued after k = nk - 4,
-  // so fewer stay outstanding.  The LDS reads of a read phase are complete
-  // (lgkmcnt 0) before its barrier.
-#define PP_WAIT(I)                                                     \
-  if (last) {                                                          \
-    if constexpr ((I) == 0) {                                          \
-      if (extra) pp_wait_n<4 + NA0 + 1>();                             \
-      else pp_wait_n<4 + NA0>();                                       \
-    } else if constexpr ((I) == 1) {                                   \
-      pp_wait_n<2>();                                                  \
-    } else if constexpr ((I) == 2) {                                   \
-      pp_wait_n<0>();                                                  \
-    }                                                                  \
-  } else if constexpr (((I) & 1) == 0) {                               \
-    if (extra) pp_wait_n<4 + NA0 + 1>();                               \
-    else pp_wait_n<4 + NA0>();                                         \
-  } else {                                                             \
-    pp_wait_n<4>();                                                    \
+// vmcnt(4 + NA + C)
+#define PP_WAIT_NA(C) wait_vmcnt<4 + NA + (C)>();
+// read phase of k-step (I), the waits of stage k + 1, the MFMA phase.  The
+// wait after the second barrier repeats the one each group made (no loads
+// are issued in between, so it returns at once); being unconditional, it
+// tells the compiler that stage k + 1 has landed, which keeps it from adding
+// waits of its own before the next LDS reads.
+#define PP_PHASES(I, XR, BR, WAIT)        \
+  read(XR, (I) & 1, BR);                  \
+  wait_lgkmcnt0();                        \
+  if (grp) { WAIT; }                      \
+  __builtin_amdgcn_sched_barrier(0);      \
+  __builtin_amdgcn_s_barrier();           \
+  __builtin_amdgcn_sched_barrier(0);      \
+  compute();                              \
+  if (!grp) { WAIT; }                     \
+  __builtin_amdgcn_sched_barrier(0);      \
+  __builtin_amdgcn_s_barrier();           \
+  __builtin_amdgcn_sched_barrier(0);      \
+  { WAIT; }
+// a step in the middle of the tile (k + 3 < nk, k != 0, k != nk - 4)
+#define PP_STEP_MID(I, XR, BR, XI, BI)                                   \
+  {                                                                      \
+    const int k = st + (I);                                              \
+    if constexpr (((I) & 1) == 0) pp_issue_a<NA>(cur, k + 2, XI, wave);   \
+    pp_issue_w(cur, k + 3, BI, wave, lane16);                            \
+    if constexpr (((I) & 1) == 0) {                                      \
+      PP_PHASES(I, XR, BR, PP_WAIT_NA(0))                                \
+    } else {                                                             \
+      PP_PHASES(I, XR, BR, wait_vmcnt<4>())                              \
+    }                                                                    \
   }
-#define PP_STEP(I, XR, BR, XI, BI)              \
-  {                                             \
-    const int k = st + (I);                     \
-    if (k >= 1 && k + 3 < nk) {                 \
-      if (((I) & 1) == 0) issue_a(k + 2, XI);   \
-      issue_w(k + 3, BI);                       \
-    }                                           \
-    read(XR, (I) & 1, BR);                      \
-    wait_lgkmcnt0();                            \
-    if (grp) { PP_WAIT(I) }                     \
-    __builtin_amdgcn_sched_barrier(0);          \
-    __builtin_amdgcn_s_barrier();               \
-    __builtin_amdgcn_sched_barrier(0);          \
-    compute();                                  \
-    if (!grp) { PP_WAIT(I) }                    \
-    __builtin_amdgcn_sched_barrier(0);          \
-    __builtin_amdgcn_s_barrier();               \
-    __builtin_amdgcn_sched_barrier(0);          \
-  }
-  for (int st = 0; st < nk; st += kStages) {
-    const bool last = st + kStages >= nk;  // the last four k-steps
-    PP_STEP(0, X0, B0, X1, B3)
-    PP_STEP(1, X0, B1, X1, B0)
-    PP_STEP(2, X1, B2, X0, B1)
-    PP_STEP(3, X1, B3, X0, B2)
-  }
-#undef PP_STEP
-#undef PP_WAIT
-  // Group 0's extra barrier pairs with group 1's last one, so both groups
-  // pass the same number of barriers per tile.
-  if constexpr (SWIGLU) {
-    // group 0 stores h while group 1 runs the last MFMAs; no LDS is read
-    // after the extra barrier, so the next tile's loads need no other one
-    gate_up_epilogue<NMBW>(g, acc, NMBW, wm, wn, nt, mrow0, mv);
-    if (!grp) __builtin_amdgcn_s_barrier();
-  } else {
-    // staging in B1/B2: every read phase ended with lgkmcnt(0) before its
-    // barrier (group 1's last one closes phase 2nk - 1) and every load was
-    // waited for, so both buffers are free
-    if (!grp) __builtin_amdgcn_s_barrier();
-    staged_epilogue<NMBW>(g, acc, NMBW, wm, wn, nt, mrow0, mv, B1, B2);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();  // staging reads done before the next tile's loads
-  }
-}
 
-// pp_tile for the instantiated height covering nmbw M-blocks per wave
-template <int N, bool SWIGLU>
-__device__ __forceinline__ void pp_dispatch(int nmbw, const FfnGroup& g, int s, int nt, int mrow0,
-                                            int mv, bf16_t* X0, bf16_t* X1, bf16_t* B0,
-                                            bf16_t* B1, bf16_t* B2, bf16_t* B3) {
-  if constexpr (N > 1) {
-    if (nmbw >= N) {
-      pp_tile<N, SWIGLU>(g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
-      return;
+  {  // step 0: the previous tile's stores may stay in flight
+    pp_issue_a<NA>(cur, 2, X1, wave);
+    pp_issue_w(cur, 3, B3, wave, lane16);
+    PP_PHASES(0, X0, B0, PP_WAIT_NA(kPPStores))
+  }
+  int st = 0;
+  PP_STEP_MID(1, X0, B1, X1, B0)
+  PP_STEP_MID(2, X1, B2, X0, B1)
+  PP_STEP_MID(3, X1, B3, X0, B2)
+  for (st = 4; st < nk - 4; st += kStages) {
+    PP_STEP_MID(0, X0, B0, X1, B3)
+    PP_STEP_MID(1, X0, B1, X1, B0)
+    PP_STEP_MID(2, X1, B2, X0, B1)
+    PP_STEP_MID(3, X1, B3, X0, B2)
+  }
+  // The last four steps (st = nk - 4) load the next tile's first stages.
+  // Without a next tile they issue the same loads over empty buffers (zeros
+  // into buffers nothing reads any more), so the code is one straight line
+  // whose loads in flight the compiler counts exactly.
+  const PPTile tc = t;
+  FfnGroup gn = pick_group(a, tc.grp);
+  {  // k = nk - 4
+    pp_issue_a<NA>(cur, st + 2, X1, wave);
+    if (has_next) {
+      t = pp_decode(a, tstart, sbeg, srows, nsegT, Ln);
+      gn = pick_group(a, t.grp);
+    } else {
+      gn.row_index = nullptr;
+      gn.a_bytes = 0u;
+      gn.w_bytes = 0u;
     }
-    pp_dispatch<N - 1, SWIGLU>(nmbw, g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
+    pp_rows_issue_lds(gn, t, wave, lane, rslot);
+    pp_issue_w(cur, st + 3, B3, wave, lane16);
+    PP_PHASES(0, X0, B0, PP_WAIT_NA(1))
+  }
+  {  // k = nk - 3: the next tile's weights
+    pp_wloads<SWIGLU>(gn, t, wave, cur);
+    pp_issue_w(cur, 0, B0, wave, lane16);
+    PP_PHASES(1, X0, B1, wait_vmcnt<5>())
+  }
+  {  // k = nk - 2: and its activations
+    // the row_index load has landed once only W(nk-1) and W'(0) may be in
+    // flight after it
+    wait_vmcnt<4>();
+    uint32_t raw[4];
+    pp_rows_read_lds(rslot, lane, raw);
+    pp_aloads(gn, t, wave, lane, raw, cur);
+    pp_issue_a<4>(cur, 0, X0, wave);
+    pp_issue_w(cur, 1, B1, wave, lane16);
+    PP_PHASES(2, X1, B2, wait_vmcnt<8>())
+  }
+  {  // k = nk - 1
+    pp_issue_w(cur, 2, B2, wave, lane16);
+    PP_PHASES(3, X1, B3, wait_vmcnt<4>())
+  }
+#undef PP_STEP_MID
+#undef PP_PHASES
+#undef PP_WAIT_NA
+
+  const FfnGroup g = pick_group(a, tc.grp);
+  if constexpr (SWIGLU) {
+    // each group right after its last MFMA phase; group 0's h stores overlap
+    // group 1's last MFMAs.  With no next tile, group 0's extra barrier
+    // pairs with group 1's last one.
+    gate_up_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv);
+    if (!has_next && !grp) __builtin_amdgcn_s_barrier();
   } else {
-    pp_tile<1, SWIGLU>(g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
+    // both groups together (group 0's extra barrier pairs with group 1's
+    // last one), staged in X1: both groups read its last stage before the
+    // barrier that ended phase 2nk - 1, and the next tile loads into it only
+    // in its first step, after the barrier that ends the epilogue
+    if (!grp) __builtin_amdgcn_s_barrier();
+    staged_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv, X1, X1 + kBuf4Elems);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    if (has_next && grp) __builtin_amdgcn_s_barrier();  // group 1 half a step behind again
   }
 }
 
 // Persistent ping-pong kernel over the tiles of both groups: rounds of
 // gridDim.x tiles, inside a round XCD x takes the x-th run of gridDim.x / 8
 // tiles (tiles sharing activation rows or weights in one L2), tile_nm order
-// inside a segment.
+// inside a segment.  The tiles of a workgroup form one stream of k-steps.
 template <bool SWIGLU>
 __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   constexpr int ROWS = kPPRows;
-  __shared__ __attribute__((aligned(16))) bf16_t X0[ROWS * 2 * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t X1[ROWS * 2 * kBK4];
-  __shared__ __attribute__((aligned(16))) bf16_t B0[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B1[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B2[kBuf4Elems];
-  __shared__ __attribute__((aligned(16))) bf16_t B3[kBuf4Elems];
+  constexpr int XE = ROWS * 2 * kBK4;  // activation buffer: two k-steps of 256 rows
+  __shared__ __attribute__((aligned(16))) bf16_t X0s[XE];
+  __shared__ __attribute__((aligned(16))) bf16_t X1s[XE];
+  __shared__ __attribute__((aligned(16))) bf16_t B0s[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B1s[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B2s[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) bf16_t B3s[kBuf4Elems];
+  __shared__ __attribute__((aligned(16))) int32_t rslots[8 * 64];  // a 256-byte row_index slot per wave
   __shared__ int tstart[kMaxSegs + 1];
+  __shared__ int sbeg[kMaxSegs];
+  __shared__ int srows[kMaxSegs];
   __shared__ int tmp[kThreads];
 
   const int nsegT = a.g[0].nseg + (a.ngroups > 1 ? a.g[1].nseg : 0);
+  for (int i = threadIdx.x; i < nsegT; i += kBigThreads) {
+    const int gi = (a.ngroups > 1 && i >= a.g[0].nseg) ? 1 : 0;
+    const FfnGroup gg = pick_group(a, gi);
+    const int s = gi ? i - a.g[0].nseg : i;
+    const int b = seg_begin(gg, s);
+    sbeg[i] = b;
+    srows[i] = seg_end(gg, s) - b;
+  }
   if (threadIdx.x < kThreads) build_tile_starts<ROWS>(a, nsegT, tstart, tmp);
   else build_tile_starts_idle();
   const int total = tstart[nsegT];
@@ -1046,27 +1263,54 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   const int per = gridDim.x / nxcd;
   const int xcd = blockIdx.x % nxcd;
   const int slot = blockIdx.x / nxcd;
-  for (int L = xcd * per + slot; L < total; L += gridDim.x) {
-    int i0 = 0, i1 = nsegT;
-    while (i1 - i0 > 1) {
-      const int mid = (i0 + i1) >> 1;
-      if (tstart[mid] <= L) i0 = mid;
-      else i1 = mid;
+  int L = xcd * per + slot;
+  if (L >= total) return;  // whole workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(static_cast<int>(threadIdx.x >> 6));
+  const int grp = wave >> 2;
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
+  int32_t* rslot = lds_opaque(rslots) + wave * 64;
+  bf16_t* X0 = lds_opaque(X0s);
+  bf16_t* X1 = lds_opaque(X1s);
+  bf16_t* B0 = lds_opaque(B0s);
+  bf16_t* B1 = lds_opaque(B1s);
+  bf16_t* B2 = lds_opaque(B2s);
+  bf16_t* B3 = lds_opaque(B3s);
+
+  PPTile t = pp_decode(a, tstart, sbeg, srows, nsegT, L);
+  PPLoads cur;
+  {
+    const FfnGroup g = pick_group(a, t.grp);
+    uint32_t raw[4];
+    pp_rows_issue(g, t, wave, lane, raw);
+    pp_wloads<SWIGLU>(g, t, wave, cur);
+    pp_aloads(g, t, wave, lane, raw, cur);
+  }
+  // the first tile's first stages, in the order a previous tile issues them;
+  // all but W(2) are waited for, so the first step's wait (which counts a
+  // previous tile's stores) is met
+  pp_issue_w(cur, 0, B0, wave, lane16);
+  pp_issue_a<4>(cur, 0, X0, wave);
+  pp_issue_w(cur, 1, B1, wave, lane16);
+  pp_issue_w(cur, 2, B2, wave, lane16);
+  wait_vmcnt<2>();
+  __builtin_amdgcn_s_barrier();
+  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
+  __builtin_amdgcn_sched_barrier(0);
+  for (;;) {
+    const int Ln = L + static_cast<int>(gridDim.x);
+    switch (t.nmbw) {
+#define PP_CASE(N)                                                                       \
+  case N:                                                                                \
+    pp_tile<N, SWIGLU>(a, tstart, sbeg, srows, nsegT, Ln, total, t, cur, X0, X1, B0, B1, \
+                       B2, B3, rslot);                                                   \
+    break;
+      PP_CASE(8) PP_CASE(7) PP_CASE(6) PP_CASE(5) PP_CASE(4) PP_CASE(3) PP_CASE(2)
+      default: PP_CASE(1)
+#undef PP_CASE
     }
-    const int grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
-    const FfnGroup g = grp ? a.g[1] : a.g[0];
-    const int s = grp ? i0 - a.g[0].nseg : i0;
-    const int r0 = seg_begin(g, s);
-    const int rows = seg_end(g, s) - r0;
-    const int mtc = (rows + ROWS - 1) / ROWS;
-    const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;
-    const int local = L - tstart[i0];
-    int nt, mt;
-    tile_nm(local, mtc, grp ? a.nt[1] : a.nt[0], nt, mt);
-    const int mrow0 = r0 + mt * rpt;
-    const int mv = min(rpt, rows - mt * rpt);
-    const int nmbw = (((mv + 15) >> 4) + 1) >> 1;
-    pp_dispatch<ROWS / 32, SWIGLU>(nmbw, g, s, nt, mrow0, mv, X0, X1, B0, B1, B2, B3);
+    if (Ln >= total) break;
+    L = Ln;
   }
 }
 
@@ -1141,10 +1385,10 @@ static hipError_t launch_big(const FfnLaunch& fl, int phase, hipStream_t st) {
   const long long ub8 = (ub + 7) / 8 * 8;
   if (grid > ub8) grid = ub8;
   grid = (grid + 7) / 8 * 8;
-  bool k128 = true;  // the ping-pong kernel consumes 4 k-steps of 32 per iteration
+  bool k128 = true;  // the ping-pong kernel: 4 k-steps of 32 per block, at least 2 blocks
   bool klong = true;
   for (int i = 0; i < fl.ngroups; ++i) {
-    k128 = k128 && fl.g[i].K % 128 == 0;
+    k128 = k128 && fl.g[i].K % 128 == 0 && fl.g[i].K >= 256;
     klong = klong && fl.g[i].K >= 1024;
   }
   // Measured (V3 prefill: gate/up K = 7168, down K = 2048; v1 and v2:
