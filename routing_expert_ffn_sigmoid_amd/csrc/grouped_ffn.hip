@@ -533,63 +533,46 @@ __device__ __forceinline__ int gate_up_epilogue(const FfnGroup& g, const f32x4 (
   return kPPStores;
 }
 
-// Down tile epilogue through LDS, so the outputs leave as whole rows.  Pass
-// p covers M-block p of both wave rows (tile rows 32p .. 32p + 31): every
-// wave writes its accumulators for those rows, rounded to bf16, into a
-// staging buffer; after a barrier each wave reads whole 1 KiB pieces of the
-// buffer and stores them, so a store instruction writes two whole 512-byte
-// rows (8 complete 128-byte lines) instead of 32-byte pieces of 16 rows, a
-// quarter of the write requests.  The 16-byte chunk c of staged row r sits
-// at position c ^ (r % 32), so the 8-byte writes of 16 rows and the row
-// reads touch distinct LDS banks.  The two staging buffers (16 KiB each,
-// free when this is called) alternate, so one barrier per pass orders the
-// writes before the reads, and the reads of pass p before the writes of
-// pass p + 2 (each wave's reads complete before its stores issue, which
-// precede its arrival at the next barrier).  Every store is issued (rows
-// past mv and columns past n_out get an offset past the buffer's bound,
-// which the hardware drops), and a short tile pads with dropped stores, so a
-// wave issues exactly kPPStores store instructions.
+// Down tile epilogue of one wave, staged through the wave's own 2 KiB LDS
+// slot so that the outputs leave as whole 128-byte row pieces: per M-block
+// the wave writes its 16 rows x 64 columns, rounded to bf16, into the slot
+// and reads them back as 8 rows x 128 bytes per instruction.  16-byte chunk
+// c of staged row r sits at position c ^ (r % 8).  LDS instructions of one
+// wave are processed in order, so a block's writes never overtake the
+// previous block's reads of the slot, and no barrier is involved: group 0
+// runs it while group 1 issues its last MFMAs, group 1 while group 0 issues
+// the next tile's first ones.  Rows past mv and columns past n_out get an
+// offset past the buffer's bound (dropped), and a short tile pads with
+// dropped stores, so a wave issues exactly kPPStores store instructions.
 template <int NJ>
-__device__ __forceinline__ int staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
-                                               int wm, int wn, int nt, int mrow0, int mv,
-                                               bf16_t* S0, bf16_t* S1) {
-  constexpr int COLS = 256;                 // output columns of a tile
-  constexpr int RB = COLS * 2;              // bytes of a staged row
-  constexpr int CPR = RB / 16;              // 16-byte chunks per staged row
-  constexpr int NI = 32 * RB / 1024;        // 1 KiB pieces per pass
-  // lane values derived here, not kept in registers across the tile
-  const int tid = static_cast<int>(opaque_u32(threadIdx.x));
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
-  const int rloc = wm * 16 + (lane & 15);   // staged row of this lane's accumulators
-  const int q = lane >> 4;                  // 4-column group inside a 16-column block
+__device__ __forceinline__ int wave_staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
+                                                    int wm, int wn, int nt, int mrow0, int mv,
+                                                    bf16_t* slot) {
+  const int lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;  // derived here
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(g.Out, g.o_bytes);
   const uint32_t ldo2 = static_cast<uint32_t>(g.ldo) * 2u;
+  char* S = reinterpret_cast<char*>(slot);
+  const int r = lane & 15;   // accumulator row of this lane
+  const int q = lane >> 4;   // 4-column group inside a 16-column block
+  const int rr = lane >> 3;  // rows rr and rr + 8 are read back
+  const int cc = lane & 7;   // 16-byte chunk read back
   u32x4 last;
 #pragma unroll
-  for (int p = 0; p < NJ; ++p) {
-    char* S = reinterpret_cast<char*>(p & 1 ? S1 : S0);
-    char* srow = S + rloc * RB;
+  for (int j = 0; j < NJ; ++j) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int col = wn * 64 + nb * 16 + q * 4;
-      const uint32_t w0 = pack_bf16x2(acc[p][nb][0], acc[p][nb][1]);
-      const uint32_t w1 = pack_bf16x2(acc[p][nb][2], acc[p][nb][3]);
-      *reinterpret_cast<u32x2*>(srow + (((col >> 3) ^ (rloc % CPR)) << 4) + ((col >> 2) & 1) * 8) =
-          u32x2{w0, w1};
+      const int c = 2 * nb + (q >> 1);
+      *reinterpret_cast<u32x2*>(S + r * 128 + ((c ^ (r & 7)) << 4) + (q & 1) * 8) =
+          u32x2{pack_bf16x2(acc[j][nb][0], acc[j][nb][1]), pack_bf16x2(acc[j][nb][2], acc[j][nb][3])};
     }
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i0 = 0; i0 < NI; i0 += 8) {
-      const int off = (i0 + wave) * 1024 + lane * 16;
-      const int r = off / RB;
-      const int c = (off % RB) >> 4;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(S + r * RB + ((c ^ (r % CPR)) << 4));
-      const int row = 32 * p + r;
-      const int col = nt * COLS + c * 8;
-      const uint32_t o = (row < mv && col < g.n_out)
-                             ? static_cast<uint32_t>(mrow0 + row) * ldo2 + static_cast<uint32_t>(col) * 2u
+    for (int i = 0; i < 2; ++i) {
+      const int row = rr + 8 * i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(S + row * 128 + ((cc ^ (row & 7)) << 4));
+      const int trow = (2 * j + wm) * 16 + row;
+      const int col = nt * 256 + wn * 64 + cc * 8;
+      const uint32_t o = (trow < mv && col < g.n_out)
+                             ? static_cast<uint32_t>(mrow0 + trow) * ldo2 + static_cast<uint32_t>(col) * 2u
                              : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_buffer_store_b128(v, ro, o, 0, 0);
       last = v;
@@ -875,11 +858,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_big_kernel(FfnLaunch a) {
 // Tiles run back to back in one stream of k-steps: the last three k-steps
 // of a tile load the first stages of the workgroup's next tile into the
 // buffers they have finished with, so a tile starts on stages already in
-// LDS, and gate/up tiles keep the half-step offset of the groups across the
-// tile boundary (group 0 stores its h while group 1 runs the last MFMAs,
-// group 1 while group 0 runs the next tile's first ones).  Down tiles (256
-// output columns) go through the staged epilogue in the activation buffer
-// that the next tile fills last.
+// LDS, and the groups keep their half-step offset across the tile boundary:
+// group 0 stores its outputs while group 1 runs the last MFMAs, group 1
+// while group 0 runs the next tile's first ones (down tiles, 256 output
+// columns, through a per-wave LDS slot, so they leave as whole rows).
 // An activation buffer holds two k-steps as 128-byte rows, so one wave's
 // activation load covers 8 whole 128-byte lines.  (Loading each k-step as
 // 64-byte rows, half of 16 lines per load, measured 6 % slower on both
@@ -1073,7 +1055,7 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
                                         const int* srows, int nsegT, int Ln, int total,
                                         PPTile& t, PPLoads& cur, bf16_t* X0, bf16_t* X1,
                                         bf16_t* B0, bf16_t* B1, bf16_t* B2, bf16_t* B3,
-                                        int32_t* rslot) {
+                                        int32_t* rslot, bf16_t* stage) {
   static_assert(NMBW >= 1 && NMBW <= 8, "tiles hold at most 256 rows");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1208,23 +1190,14 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
 #undef PP_WAIT_NA
 
   const FfnGroup g = pick_group(a, tc.grp);
-  if constexpr (SWIGLU) {
-    // each group right after its last MFMA phase; group 0's h stores overlap
-    // group 1's last MFMAs.  With no next tile, group 0's extra barrier
-    // pairs with group 1's last one.
-    gate_up_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv);
-    if (!has_next && !grp) __builtin_amdgcn_s_barrier();
-  } else {
-    // both groups together (group 0's extra barrier pairs with group 1's
-    // last one), staged in X1: both groups read its last stage before the
-    // barrier that ended phase 2nk - 1, and the next tile loads into it only
-    // in its first step, after the barrier that ends the epilogue
-    if (!grp) __builtin_amdgcn_s_barrier();
-    staged_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv, X1, X1 + kBuf4Elems);
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (has_next && grp) __builtin_amdgcn_s_barrier();  // group 1 half a step behind again
-  }
+  // each group right after its last MFMA phase: group 0's stores overlap
+  // group 1's last MFMAs, group 1's the next tile's first MFMAs of group 0
+  // (the groups stage down tiles in the same four slots, one phase apart:
+  // group 0's slot reads complete before the barrier that ends that phase).
+  // With no next tile, group 0's extra barrier pairs with group 1's last one.
+  if constexpr (SWIGLU) gate_up_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv);
+  else wave_staged_epilogue<NMBW>(g, acc, wm, wn, tc.nt, tc.mrow0, tc.mv, stage);
+  if (!has_next && !grp) __builtin_amdgcn_s_barrier();
 }
 
 // Persistent ping-pong kernel over the tiles of both groups: rounds of
@@ -1242,6 +1215,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   __shared__ __attribute__((aligned(16))) bf16_t B2s[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) bf16_t B3s[kBuf4Elems];
   __shared__ __attribute__((aligned(16))) int32_t rslots[8 * 64];  // a 256-byte row_index slot per wave
+  __shared__ __attribute__((aligned(16))) bf16_t stages[SWIGLU ? 8 : 4 * 1024];  // down: 2 KiB per wave of a group
   __shared__ int tstart[kMaxSegs + 1];
   __shared__ int sbeg[kMaxSegs];
   __shared__ int srows[kMaxSegs];
@@ -1270,6 +1244,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
   const int grp = wave >> 2;
   const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
   int32_t* rslot = lds_opaque(rslots) + wave * 64;
+  bf16_t* stage = lds_opaque(stages) + (SWIGLU ? 0 : (wave & 3) * 1024);
   bf16_t* X0 = lds_opaque(X0s);
   bf16_t* X1 = lds_opaque(X1s);
   bf16_t* B0 = lds_opaque(B0s);
@@ -1303,7 +1278,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
 #define PP_CASE(N)                                                                       \
   case N:                                                                                \
     pp_tile<N, SWIGLU>(a, tstart, sbeg, srows, nsegT, Ln, total, t, cur, X0, X1, B0, B1, \
-                       B2, B3, rslot);                                                   \
+                       B2, B3, rslot, stage);                                            \
     break;
       PP_CASE(8) PP_CASE(7) PP_CASE(6) PP_CASE(5) PP_CASE(4) PP_CASE(3) PP_CASE(2)
       default: PP_CASE(1)
