@@ -1084,6 +1084,23 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
     for (int j = 0; j < NMBW; ++j)
       af[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + j * 32 * (2 * kBK4)));
   };
+  // fragment reads LO .. HI - 1 of a k-step (weight blocks 0-3, then
+  // activation blocks), for interleaving with the direct-load issue
+  auto read_part = [&](const bf16_t* Xb, int half, const bf16_t* Bb, auto lo_c, auto hi_c)
+                       __attribute__((always_inline)) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+    const bf16_t* abase = Xb + arow + (((half * 4 + (lane >> 4)) ^ swz) * 8);
+#pragma unroll
+    for (int i = 0; i < 4 + NMBW; ++i) {
+      if (i >= LO && i < HI) {
+        if (i < 4)
+          bf[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              Bb + lane * 8 + big_wblock<SWIGLU>(wn, i) * kTileElems));
+        else
+          af[i - 4] = as_bf16x8(*reinterpret_cast<const u32x4*>(abase + (i - 4) * 32 * (2 * kBK4)));
+      }
+    }
+  };
   f32x4 acc[NMBW][4];
 #pragma unroll
   for (int j = 0; j < NMBW; ++j)
@@ -1117,17 +1134,57 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
   __builtin_amdgcn_s_barrier();           \
   __builtin_amdgcn_sched_barrier(0);      \
   { WAIT; }
-// a step in the middle of the tile (k + 3 < nk, k != 0, k != nk - 4)
-#define PP_STEP_MID(I, XR, BR, XI, BI)                                   \
-  {                                                                      \
-    const int k = st + (I);                                              \
-    if constexpr (((I) & 1) == 0) pp_issue_a<NA>(cur, k + 2, XI, wave);   \
-    pp_issue_w(cur, k + 3, BI, wave, lane16);                            \
-    if constexpr (((I) & 1) == 0) {                                      \
-      PP_PHASES(I, XR, BR, PP_WAIT_NA(0))                                \
-    } else {                                                             \
-      PP_PHASES(I, XR, BR, wait_vmcnt<4>())                              \
-    }                                                                    \
+#define PP_PHASES_NOREAD(WAIT)            \
+  wait_lgkmcnt0();                        \
+  if (grp) { WAIT; }                      \
+  __builtin_amdgcn_sched_barrier(0);      \
+  __builtin_amdgcn_s_barrier();           \
+  __builtin_amdgcn_sched_barrier(0);      \
+  compute();                              \
+  if (!grp) { WAIT; }                     \
+  __builtin_amdgcn_sched_barrier(0);      \
+  __builtin_amdgcn_s_barrier();           \
+  __builtin_amdgcn_sched_barrier(0);      \
+  { WAIT; }
+  using IC0 = std::integral_constant<int, 0>;
+  constexpr int RA = 4 + NMBW;  // fragment reads per step
+  // even step: each activation load followed by a share of the reads, then
+  // the weight loads; odd step: weight load, half the reads, weight load, rest
+#define PP_STEP_MID(I, XR, BR, XI, BI)                                              \
+  {                                                                                 \
+    const int k = st + (I);                                                         \
+    if constexpr (((I) & 1) == 0) {                                                 \
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(cur.a_base, cur.a_bytes);         \
+      const uint32_t kb = static_cast<uint32_t>(k + 2) * (kBK4 * 2);                \
+      constexpr int P = (RA + NA - 1) / NA;                                         \
+      dma16(ra, cur.aoff[0], kb, XI + (0 * 8 + wave) * 8 * (2 * kBK4));             \
+      read_part(XR, (I) & 1, BR, IC0{}, std::integral_constant<int, (P < RA ? P : RA)>{}); \
+      if constexpr (NA > 1) {                                                       \
+        dma16(ra, cur.aoff[1], kb, XI + (1 * 8 + wave) * 8 * (2 * kBK4));           \
+        read_part(XR, (I) & 1, BR, std::integral_constant<int, (P < RA ? P : RA)>{},  \
+                  std::integral_constant<int, (2 * P < RA ? 2 * P : RA)>{});        \
+      }                                                                             \
+      if constexpr (NA > 2) {                                                       \
+        dma16(ra, cur.aoff[2], kb, XI + (2 * 8 + wave) * 8 * (2 * kBK4));           \
+        read_part(XR, (I) & 1, BR, std::integral_constant<int, (2 * P < RA ? 2 * P : RA)>{}, \
+                  std::integral_constant<int, (3 * P < RA ? 3 * P : RA)>{});        \
+      }                                                                             \
+      if constexpr (NA > 3) {                                                       \
+        dma16(ra, cur.aoff[3], kb, XI + (3 * 8 + wave) * 8 * (2 * kBK4));           \
+      }                                                                             \
+      read_part(XR, (I) & 1, BR, std::integral_constant<int, ((NA > 3 ? 3 : NA) * P < RA ? (NA > 3 ? 3 : NA) * P : RA)>{}, \
+                std::integral_constant<int, RA>{});                                 \
+      pp_issue_w(cur, k + 3, BI, wave, lane16);                                     \
+      PP_PHASES_NOREAD(PP_WAIT_NA(0))                                               \
+    } else {                                                                        \
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(cur.w_base, cur.w_bytes);         \
+      const uint32_t kw = static_cast<uint32_t>(k + 3) * 1024u;                     \
+      dma16(rb, lane16, cur.wrow0 + kw, BI + wave * kTileElems);                    \
+      read_part(XR, (I) & 1, BR, IC0{}, std::integral_constant<int, RA / 2>{});     \
+      dma16(rb, lane16, cur.wrow1 + kw, BI + (8 + wave) * kTileElems);              \
+      read_part(XR, (I) & 1, BR, std::integral_constant<int, RA / 2>{}, std::integral_constant<int, RA>{}); \
+      PP_PHASES_NOREAD(wait_vmcnt<4>())                                             \
+    }                                                                               \
   }
 
   {  // step 0: the previous tile's stores may stay in flight
@@ -1187,6 +1244,7 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
   }
 #undef PP_STEP_MID
 #undef PP_PHASES
+#undef PP_PHASES_NOREAD
 #undef PP_WAIT_NA
 
   const FfnGroup g = pick_group(a, tc.grp);
