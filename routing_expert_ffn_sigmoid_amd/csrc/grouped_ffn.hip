@@ -882,26 +882,31 @@ struct PPTile {
   int grp, s, nt, mrow0, mv, nmbw, nk;
 };
 
-// Tile L of the flat tile list: segment by binary search over the tile
-// starts, rows from the segment table, both in LDS (no memory instruction,
-// so nothing enters the count of loads in flight).
+// Tile L of the flat tile list: its segment is the last one whose first
+// tile is <= L, found by the whole wave in two rounds of LDS reads (lane l
+// compares entry 16 l, then entries 16 h .. 16 h + 15 after the last lane h
+// that passed; the tile starts do not decrease, so the lanes that pass form
+// a prefix), rows from the segment table; all in LDS, so no memory
+// instruction enters the count of loads in flight.
 __device__ __forceinline__ PPTile pp_decode(const FfnLaunch& a, const int* tstart,
                                             const int* sbeg, const int* srows, int nsegT, int L) {
-  int i0 = 0, i1 = nsegT;
-  while (i1 - i0 > 1) {
-    const int mid = (i0 + i1) >> 1;
-    if (tstart[mid] <= L) i0 = mid;
-    else i1 = mid;
-  }
-  i0 = wave_uniform(i0);
+  static_assert(kMaxSegs <= 64 * 16, "two rounds of 64 lanes cover the segments");
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  const int i1 = lane * 16;
+  const uint64_t m1 = __ballot(i1 < nsegT && tstart[i1] <= L);  // lane 0 always (tstart[0] = 0)
+  const int h = 63 - __clzll(static_cast<long long>(m1));
+  const int i2 = h * 16 + (lane & 15);
+  const uint64_t m2 = __ballot(lane < 16 && i2 < nsegT && tstart[i2] <= L);
+  const int i0 = wave_uniform(h * 16 + 63 - __clzll(static_cast<long long>(m2)));
+  const int b0 = sbeg[i0], n0 = srows[i0], f0 = tstart[i0];  // three reads in flight together
   PPTile t;
   t.grp = (a.ngroups > 1 && i0 >= a.g[0].nseg) ? 1 : 0;
   t.s = t.grp ? i0 - a.g[0].nseg : i0;
-  const int r0 = wave_uniform(sbeg[i0]);
-  const int rows = wave_uniform(srows[i0]);
+  const int r0 = wave_uniform(b0);
+  const int rows = wave_uniform(n0);
   const int mtc = (rows + kPPRows - 1) / kPPRows;
   const int rpt = ((rows + mtc - 1) / mtc + 15) & ~15;  // balanced rows per tile
-  const int local = L - wave_uniform(tstart[i0]);
+  const int local = L - wave_uniform(f0);
   int mt;
   tile_nm(local, mtc, t.grp ? a.nt[1] : a.nt[0], t.nt, mt);
   t.mrow0 = r0 + mt * rpt;
