@@ -250,7 +250,7 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
     lines = [f"# rocprofv3 summary: DeepSeekMoE layer forward, workload {workload}", "",
              f"library code object (gfx950) holding the gate/up kernel: "
              f"{code_object_digest(GATE_UP_KERNEL)}"]
-    for key in ("trace", "fetch", "write", "copy_fetch", "copy_write"):
+    for key in ("trace", "fetch", "write", "copy_fetch", "copy_write", "clock"):
         if key in commands:
             lines.append(f"{key}: {commands[key]}")
     lines += ["", "## kernel trace (--kernel-trace --stats), library kernels, all calls",
@@ -328,6 +328,23 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
         wb = write.get(k, 0.0) * 1024 * (w_scale or 1.0)
         traffic[k] = fb + wb
         lines.append(f"{k:60s} {fetch.get(k, 0.0):14.1f} {write.get(k, 0.0):12.1f} {fb + wb:16.4g}")
+    # shader clock during each launch: GRBM_GUI_ACTIVE (GPU-busy cycles of
+    # the graphics clock) over the dispatch's own duration in the same run
+    clk = {}
+    for r in _csv_rows(os.path.join(d, "clock", "**", "*counter_collection.csv")):
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE" or "moe::" not in r["Kernel_Name"]:
+            continue
+        k = r["Kernel_Name"].replace("void ", "").split("(")[0]
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if ns > 0:
+            clk.setdefault(k, []).append((float(r["Counter_Value"]), ns))
+    if clk:
+        lines += ["", "## shader clock per launch (GRBM_GUI_ACTIVE cycles / launch duration, same run)",
+                  f"{'kernel':60s} {'launches':>8s} {'MHz':>8s}"]
+        for k in sorted(clk, key=lambda n: -sum(ns for _, ns in clk[n])):
+            cyc = sum(c for c, _ in clk[k])
+            ns = sum(n for _, n in clk[k])
+            lines.append(f"{k:60s} {len(clk[k]):8d} {1e3 * cyc / ns:8.0f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
     with open(txt, "w") as fh:
@@ -528,7 +545,8 @@ def main():
                     "fetch": cmd.format(opt="--pmc FETCH_SIZE", args=pmc),
                     "write": cmd.format(opt="--pmc WRITE_SIZE", args=pmc),
                     "copy_fetch": cmd.format(opt="--pmc FETCH_SIZE", args="--calibrate-copy"),
-                    "copy_write": cmd.format(opt="--pmc WRITE_SIZE", args="--calibrate-copy")}
+                    "copy_write": cmd.format(opt="--pmc WRITE_SIZE", args="--calibrate-copy"),
+                    "clock": cmd.format(opt="--pmc GRBM_GUI_ACTIVE", args=pmc)}
         summarize_profile(args.summarize_profile, args.workload, commands, args.steps)
         return
     if args.gpus != 1:

@@ -206,11 +206,12 @@ def test_bf16_small_layer_parity_and_determinism():
                                                    (600, 1024, 384)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height.
-    Large segments run the gate/up projection (K = H, a multiple of 128,
-    from 128 = four k-steps, all in the kernel's last loop iteration, up to
-    4096 here) on the ping-pong kernel; expert widths of 1024, 1408 and 2048
-    send the down projection there too (K >= 1024; with H = 384 or 448 its
-    second column tile is partial), 128-256 through the 2-stage kernel."""
+    Large segments run the gate/up projection on the ping-pong kernel when
+    K = H is a multiple of 128 from 256 (eight k-steps: only its first and
+    last blocks of four) up to 4096 here, on the 2-stage kernel for H = 128
+    and 448; expert widths of 1024, 1408 and 2048 send the down projection to
+    the ping-pong kernel too (K >= 1024; with H = 384 its second column tile
+    is partial), 128-256 through the 2-stage kernel."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
     nseg = 9
