@@ -611,6 +611,12 @@ def main():
                      "code_object": code_object_digest(GATE_UP_KERNEL),
                      "beside": secondary})
     layer_tflops = work["layer_flop"] / (ms_per_step / 1e3) / 1e12
+    # the whole layer against the same MFMA peak (all of the step's flop over
+    # the step time), kept inside the roofline object next to the kernel's
+    roofline["layer"] = {"bound": "mfma", "achieved": round(layer_tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(layer_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "flop": work["layer_flop"], "ms": round(ms_per_step, 4)}
     tb = touched_weight_bytes(wl, touched)
 
     res = {
