@@ -186,14 +186,25 @@ __global__ __launch_bounds__(256) void router_pieces_kernel(const WT* __restrict
 
 // GEMM: a workgroup of 8 waves owns 256 tokens x 256 experts of one K split;
 // wave (wm, wn) = (wave & 1, wave >> 1) owns token blocks 2j + wm (j < 8) and
-// expert blocks 4wn .. 4wn+3 (16 x 16 each).  k-steps of 32, two LDS stages,
-// both operands loaded global -> LDS directly:
+// expert blocks 4wn .. 4wn+3 (16 x 16 each).  k-steps of 32 in two LDS
+// stages, both operands loaded global -> LDS directly:
 //   tokens: 256 rows x 64 B per step, 16-byte chunks XOR-swizzled by row
 //           pairs (physical chunk = logical ^ ((row >> 1) & 3));
 //   pieces: np x 16 expert blocks of 1 KiB per step, already in fragment
 //           order.
+// Ping-pong schedule: waves 0-3 (expert blocks 0-7, group 0) and waves 4-7
+// (blocks 8-15, group 1; the dispatcher puts waves w and w + 4 on one SIMD)
+// run half a k-step apart.  In every phase (closed by a workgroup barrier)
+// one group reads a k-step's fragments from LDS while the other issues that
+// k-step's 32 np MFMAs back to back, so each matrix core is fed by one wave
+// at a time with no LDS waits between its MFMAs.  Group 0 issues all of the
+// next stage's loads at the start of its read phase, into the stage both
+// groups finished reading by the barrier before, and waits for them after
+// its MFMA phase, before the barrier after which it reads them (group 1
+// reads them one phase later); group 1 issues no loads.
 // MFMA operands are (weights, tokens), so a lane's accumulator holds four
-// consecutive experts of one token: 16-byte partial stores.
+// consecutive experts of one token: 16-byte partial stores, group 0's while
+// group 1 issues its last MFMAs.
 constexpr int kRtRows = 256;
 constexpr int kRtThreads = 512;
 constexpr int kRtAElems = kRtRows * 32;  // one stage of token rows
@@ -212,6 +223,8 @@ __global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t B1[NP * kRtBElems];
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(static_cast<int>(threadIdx.x >> 6));
+  const int grp = wave >> 2;
+  const int gw = wave & 3;  // wave within its group
   const int wm = wave & 1, wn = wave >> 1;
   const int t0 = blockIdx.x * kRtRows;
   const int eb = blockIdx.y * 16;  // first expert block of the tile
@@ -220,18 +233,19 @@ __global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
   const int k1 = min(nkb, k0 + ksteps);
   const int nblk = npad / 16;
 
-  // token rows: wave copies row groups q*8 + wave (16 rows, 1 KiB) per step
+  // group 0's loads: token row groups q*4 + gw (16 rows, 1 KiB; lane ->
+  // row 16 g + lane/4, chunk lane%4), piece blocks b = q*4 + gw (piece b/16,
+  // expert block b%16)
   const int rows = min(kRtRows, T - t0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(
       x + static_cast<int64_t>(t0) * H, static_cast<uint32_t>(rows) * static_cast<uint32_t>(H) * 2u);
   const int logical = (lane & 3) ^ ((lane >> 3) & 3);
-  uint32_t aoff[2];
+  uint32_t aoff[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = (q * 8 + wave) * 16 + (lane >> 2);
+  for (int q = 0; q < 4; ++q) {
+    const int row = (q * 4 + gw) * 16 + (lane >> 2);
     aoff[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(H) * 2u + logical * 16u;
   }
-  // pieces: wave copies blocks b = q*8 + wave (piece b/16, expert block b%16)
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(pieces, static_cast<uint32_t>(NP) * static_cast<uint32_t>(npad) *
                             static_cast<uint32_t>(H) * 2u);
@@ -239,11 +253,11 @@ __global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
 
   auto issue = [&](int kb, bf16_t* Ab, bf16_t* Bb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      dma16(rx, aoff[q], static_cast<uint32_t>(kb) * 64u, Ab + (q * 8 + wave) * 512);
+    for (int q = 0; q < 4; ++q)
+      dma16(rx, aoff[q], static_cast<uint32_t>(kb) * 64u, Ab + (q * 4 + gw) * 512);
 #pragma unroll
-    for (int q = 0; q < 2 * NP; ++q) {
-      const int b = q * 8 + wave;
+    for (int q = 0; q < 4 * NP; ++q) {
+      const int b = q * 4 + gw;
       const int blk = eb + (b & 15);
       if (blk < nblk)  // wave-uniform
         dma16(rw, lane * 16u,
@@ -264,9 +278,8 @@ __global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
   const int ch = (lane >> 4) ^ (((lane & 15) >> 1) & 3);
   const int aread = (wm * 16 + (lane & 15)) * 32 + ch * 8;
   const int bread = (4 * wn) * 512 + lane * 8;
-
-  auto compute = [&](const bf16_t* Ab, const bf16_t* Bb) {
-    bf16x8 bf[NP][4];
+  bf16x8 af[8], bf[NP][4];
+  auto read = [&](const bf16_t* Ab, const bf16_t* Bb) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -274,44 +287,58 @@ __global__ __launch_bounds__(kRtThreads, 1) void router_bf16_kernel(
         bf[p][nb] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(Bb + p * kRtBElems + bread + nb * 512));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 af =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ab + aread + j * 32 * 32));
+    for (int j = 0; j < 8; ++j)
+      af[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ab + aread + j * 32 * 32));
+  };
+  auto mfma = [&]() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int p = NP - 1; p >= 0; --p)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[p][nb], af, acc[j][nb], 0, 0, 0);
-    }
+          acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[p][nb], af[j], acc[j][nb], 0, 0, 0);
   };
-  // step kb computes from (Ac, Bc) and loads step kb + 1 into (An, Bn).
-  // Waiting for this wave's loads and crossing the barrier makes every
-  // wave's loads of step kb visible, and tells that no wave still reads the
-  // buffer the next loads overwrite.
+  // step kb reads (Ac, Bc); group 0 first issues step kb + 1 into (An, Bn)
   auto step = [&](int kb, const bf16_t* Ac, const bf16_t* Bc, bf16_t* An, bf16_t* Bn) {
-    wait_vmcnt<0>();
+    if (grp == 0 && kb + 1 < k1) issue(kb + 1, An, Bn);
+    if (active) read(Ac, Bc);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
-    if (kb + 1 < k1) issue(kb + 1, An, Bn);
-    if (active) compute(Ac, Bc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (active) mfma();
+    if (grp == 0) wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(k0, A0, B0);
+  if (grp == 0) {
+    issue(k0, A0, B0);
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  if (grp) __builtin_amdgcn_s_barrier();  // group 1 starts one phase later
   for (int kb = k0; kb < k1; kb += 2) {
     step(kb, A0, B0, A1, B1);
     if (kb + 1 < k1) step(kb + 1, A1, B1, A0, B0);
   }
-  if (!active) return;
   // D layout: lane holds experts 4*(lane/16) .. +3 of token lane%16
-  float* out = part + static_cast<int64_t>(blockIdx.z) * T * N;
+  if (active) {
+    float* out = part + static_cast<int64_t>(blockIdx.z) * T * N;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = t0 + (2 * j + wm) * 16 + (lane & 15);
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + (2 * j + wm) * 16 + (lane & 15);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int e = (eb + 4 * wn + nb) * 16 + 4 * (lane >> 4);
-      if (t < T && e < N) *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * N + e) = acc[j][nb];
+      for (int nb = 0; nb < 4; ++nb) {
+        const int e = (eb + 4 * wn + nb) * 16 + 4 * (lane >> 4);
+        if (t < T && e < N) *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * N + e) = acc[j][nb];
+      }
     }
   }
+  // group 0's extra barrier pairs with group 1's last one
+  if (grp == 0) __builtin_amdgcn_s_barrier();
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
