@@ -339,12 +339,19 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
         if ns > 0:
             clk.setdefault(k, []).append((float(r["Counter_Value"]), ns))
     if clk:
-        lines += ["", "## shader clock per launch (GRBM_GUI_ACTIVE cycles / launch duration, same run)",
+        # the counter is summed over the GPU's XCDs (one graphics engine each)
+        nxcc = 1
+        for r in _csv_rows(os.path.join(d, "clock", "**", "*agent_info.csv")):
+            if r.get("Agent_Type") == "GPU" and int(r.get("Num_Xcc", 0) or 0) > 0:
+                nxcc = int(r["Num_Xcc"])
+        lines += ["", "## shader clock per launch (GRBM_GUI_ACTIVE summed over the "
+                  f"{nxcc} XCDs / {nxcc} / launch duration, same run; launches of a few tens of "
+                  "microseconds read high: the counter also runs outside the kernel's timestamps)",
                   f"{'kernel':60s} {'launches':>8s} {'MHz':>8s}"]
         for k in sorted(clk, key=lambda n: -sum(ns for _, ns in clk[n])):
             cyc = sum(c for c, _ in clk[k])
             ns = sum(n for _, n in clk[k])
-            lines.append(f"{k:60s} {len(clk[k]):8d} {1e3 * cyc / ns:8.0f}")
+            lines.append(f"{k:60s} {len(clk[k]):8d} {1e3 * cyc / ns / nxcc:8.0f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
     with open(txt, "w") as fh:
