@@ -473,7 +473,6 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
 // addresses it can trace, the compiler adds waits of its own before the
 // reads, counted for the most cautious path through the kernel's loops,
 // which hold back loads and stores the reads do not depend on.
-typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
 template <typename T>
 __device__ __forceinline__ T* lds_opaque(T* p) {
   __attribute__((address_space(3))) T* q = (__attribute__((address_space(3))) T*)p;
@@ -1357,7 +1356,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void ffn_pp_kernel(FfnLaunch a) {
 // and the workgroup's first wave writes all eight to simd[8g .. 8g + 7].
 // The ping-pong schedule's speed relies on waves w and w + 4 sharing a SIMD
 // (its correctness does not: barriers order every access).  Same launch
-// shape and LDS footprint as ffn_pp_kernel, so one workgroup per CU.
+// shape as ffn_pp_kernel, and like it enough LDS (its stage buffers) that
+// one workgroup holds a CU.
 constexpr int kPPLdsInts = (2 * kPPRows * 2 * kBK4 + kStages * kBuf4Elems) / 2;
 __global__ __launch_bounds__(kBigThreads, 1) void wave_simd_kernel(int32_t* __restrict__ simd) {
   __shared__ int32_t ids[kPPLdsInts];
