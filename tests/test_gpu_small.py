@@ -203,7 +203,7 @@ def test_bf16_small_layer_parity_and_determinism():
                                                    (400, 2048, 256), (150, 2048, 448),
                                                    (150, 128, 128), (150, 256, 4096),
                                                    (300, 128, 4096), (150, 1408, 256),
-                                                   (600, 1024, 384)])
+                                                   (600, 1024, 384), (700, 2048, 256)])
 def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     """moe_grouped_ffn alone: ragged and empty segments, every tile height.
     Large segments run the gate/up projection on the ping-pong kernel when
@@ -211,7 +211,9 @@ def test_grouped_ffn_ragged_segments(rows_per_seg, inter, H):
     last blocks of four) up to 4096 here, on the 2-stage kernel for H = 128
     and 448; expert widths of 1024, 1408 and 2048 send the down projection to
     the ping-pong kernel too (K >= 1024; with H = 384 its second column tile
-    is partial), 128-256 through the 2-stage kernel."""
+    is partial), 128-256 through the 2-stage kernel.  The last case has more
+    gate/up tiles than workgroups at eight k-steps per tile, so tiles of
+    different heights follow each other in one workgroup's stream."""
     require_gpu()
     rng = np.random.default_rng(rows_per_seg)
     nseg = 9
