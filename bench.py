@@ -250,7 +250,7 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
     lines = [f"# rocprofv3 summary: DeepSeekMoE layer forward, workload {workload}", "",
              f"library code object (gfx950) holding the gate/up kernel: "
              f"{code_object_digest(GATE_UP_KERNEL)}"]
-    for key in ("trace", "fetch", "write", "copy_fetch", "copy_write", "clock"):
+    for key in ("trace", "fetch", "write", "copy_fetch", "copy_write", "clock", "tcp"):
         if key in commands:
             lines.append(f"{key}: {commands[key]}")
     lines += ["", "## kernel trace (--kernel-trace --stats), library kernels, all calls",
@@ -352,6 +352,31 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
             cyc = sum(c for c, _ in clk[k])
             ns = sum(n for _, n in clk[k])
             lines.append(f"{k:60s} {len(clk[k]):8d} {1e3 * cyc / ns / nxcc:8.0f}")
+    # vector L1 -> L2 requests of the large kernels (per-CU counters summed
+    # over the CUs), with GRBM_GUI_ACTIVE of the same run for the cycles
+    tcp = {}
+    for r in _csv_rows(os.path.join(d, "tcp", "**", "*counter_collection.csv")):
+        if "moe::" not in r["Kernel_Name"]:
+            continue
+        k = r["Kernel_Name"].replace("void ", "").split("(")[0]
+        tcp.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if tcp:
+        ncu, nxcc = 0, 1
+        for r in _csv_rows(os.path.join(d, "tcp", "**", "*agent_info.csv")):
+            if r.get("Agent_Type") == "GPU":
+                ncu = int(r.get("Cu_Count", 0) or 0)
+                nxcc = max(1, int(r.get("Num_Xcc", 1) or 1))
+        lines += ["", f"## vector L1 -> L2 reads per launch ({ncu} CUs; per-CU counters summed)",
+                  f"{'kernel':60s} {'reads':>12s} {'avg latency':>12s} {'pending-stall':>14s}"]
+        for k in sorted(tcp, key=lambda n: -max(tcp[n].get("TCP_TCC_READ_REQ_sum", [0]))):
+            c = {n: sum(v) / len(v) for n, v in tcp[k].items()}
+            req = c.get("TCP_TCC_READ_REQ_sum", 0.0)
+            lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / req if req else 0.0
+            cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / nxcc  # graphics-clock cycles of the launch
+            stall = c.get("TCP_PENDING_STALL_CYCLES_sum", 0.0) / (ncu * cyc) if ncu and cyc else 0.0
+            if req < 1e6:
+                continue
+            lines.append(f"{k:60s} {req:12.4g} {lat:10.0f} cy {100 * stall:12.1f} %")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     txt = os.path.join(ROOT, "profiles", f"layer_kernels_{workload}.txt")
     with open(txt, "w") as fh:
@@ -553,7 +578,9 @@ def main():
                     "write": cmd.format(opt="--pmc WRITE_SIZE", args=pmc),
                     "copy_fetch": cmd.format(opt="--pmc FETCH_SIZE", args="--calibrate-copy"),
                     "copy_write": cmd.format(opt="--pmc WRITE_SIZE", args="--calibrate-copy"),
-                    "clock": cmd.format(opt="--pmc GRBM_GUI_ACTIVE", args=pmc)}
+                    "clock": cmd.format(opt="--pmc GRBM_GUI_ACTIVE", args=pmc),
+                    "tcp": cmd.format(opt="--pmc TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum "
+                                          "TCP_PENDING_STALL_CYCLES_sum GRBM_GUI_ACTIVE", args=pmc)}
         summarize_profile(args.summarize_profile, args.workload, commands, args.steps)
         return
     if args.gpus != 1:
