@@ -8,7 +8,7 @@ constant plus one would leave a needed load in flight.
 The order modelled (one wave; NA = ceil(4 * NMBW / 8) activation loads per
 pair of k-steps, 2 weight loads per k-step, 1 row_index load, 16 epilogue
 stores):
-  first tile:  W(0), A(0,1), W(1), W(2); wait vmcnt(2)
+  first tile:  W(0), A(0,1) (4 loads), W(1), W(2); wait vmcnt(2)
   step k:      k + 3 < nk: A(k+2,k+3) if k even, R at k = nk-4, W(k+3)
                otherwise:  W'(0) | A'(0,1) (4 loads), W'(1) | W'(2)
   after a tile: 16 stores
@@ -54,8 +54,7 @@ def run(tiles, delta=None):
     def stage(ti, j):
         return {(f"W{j}", ti), (f"A{j - j % 2}", ti)}
 
-    na0 = (4 * tiles[0][1] + 7) // 8
-    issue("W0", 0, 2); issue("A0", 0, na0); issue("W1", 0, 2); issue("W2", 0, 2)
+    issue("W0", 0, 2); issue("A0", 0, 4); issue("W1", 0, 2); issue("W2", 0, 2)
     wait(2, stage(0, 0) | {("W1", 0)}, "prologue")
     for ti, (nk, nmbw) in enumerate(tiles):
         na = (4 * nmbw + 7) // 8
