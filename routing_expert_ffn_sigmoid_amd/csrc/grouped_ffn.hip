@@ -1110,12 +1110,22 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
   for (int j = 0; j < NMBW; ++j)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // with an odd number of 16-row blocks the last block of the odd-parity
+  // waves lies past the tile's rows: they skip its MFMAs (nothing of it is
+  // stored)
+  const bool skip_last = wm == 1 && ((((t.mv + 15) >> 4) & 1) != 0);
   auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NMBW; ++j)
+    for (int j = 0; j < NMBW - 1; ++j)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[j], acc[j][nb], 0, 0, 0);
+    if (!skip_last) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[NMBW - 1][nb] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[nb], af[NMBW - 1], acc[NMBW - 1][nb], 0, 0, 0);
+    }
   };
 
 // vmcnt(4 + NA + C)
