@@ -491,15 +491,39 @@ __device__ __forceinline__ uint32_t swiglu_pack(float g0, float g1, float u0, fl
 }
 
 // Stores a tile epilogue issues per wave, whatever the tile's height: the
-// count the next tile's first wait is built from.
-constexpr int kPPStores = 16;
+// count the next tile's first wait is built from (gate/up: one per M-block
+// of the tallest tile, down: two).
+template <bool SWIGLU>
+constexpr int kPPStores = SWIGLU ? 8 : 16;
 
-// Gate/up tile epilogue straight from registers: per M-block and lane, h of
-// 4 consecutive columns of one row (8 bytes) for each of the wave's two
-// 16-column blocks.  Every store is issued (a lane whose row lies past mv or
-// whose columns lie past n_out gets an offset past the buffer's bound, which
-// the hardware drops), and a short tile pads with dropped stores, so a wave
-// issues exactly kPPStores store instructions.  The buffer bound (o_bytes)
+// Lane swaps between two registers (gfx950): swap32 exchanges a's lanes
+// 32-63 with b's lanes 0-31, swap16 a's odd 16-lane rows with b's even ones.
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Cache-policy bits of the h stores: device scope (sc1).  Measured against
+// the default on V3 prefill, alternating in one process: the gate/up launch
+// 1-1.5 % faster (the y stores of the down launch gain nothing from it).
+constexpr int kStoreDeviceScope = 16;
+
+// Gate/up tile epilogue straight from registers.  Per M-block a lane holds,
+// for row r = lane % 16, h of columns 16 nb + 4 q .. + 3 (q = lane / 16) of
+// the wave's two 16-column blocks nb, one 8-byte word each.  A swap of lane
+// bit 5 with nb, then of lane bit 4 with nb, leaves lane (r, q) with the
+// words of columns 8 q .. 8 q + 7, stored as one 16-byte piece: each store
+// instruction writes 64 contiguous bytes (the wave's 32 columns) of each of
+// 16 rows.  Every store is issued (a lane whose row lies past mv or whose
+// columns lie past n_out gets an offset past the buffer's bound, which the
+// hardware drops), and the count is padded with dropped stores, so a wave
+// issues exactly kPPStores<true> store instructions.  The buffer bound (o_bytes)
 // is at most 0xFFFFFF00, so a dropped offset never wraps.
 template <int NJ>
 __device__ __forceinline__ int gate_up_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
@@ -507,29 +531,35 @@ __device__ __forceinline__ int gate_up_epilogue(const FfnGroup& g, const f32x4 (
   const int lane = static_cast<int>(opaque_u32(threadIdx.x)) & 63;  // derived here
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(g.Out, g.o_bytes);
   const int rl = lane & 15;
-  const int cq = (lane >> 4) * 4;
+  const int col = nt * 128 + wn * 32 + (lane >> 4) * 8;
   const uint32_t ldo2 = static_cast<uint32_t>(g.ldo) * 2u;
-  u32x2 last;
+  u32x4 last;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int r = (2 * j + wm) * 16 + rl;
-    const uint32_t rowoff = static_cast<uint32_t>(mrow0 + r) * ldo2;
+    uint32_t w[2][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int col = nt * 128 + wn * 32 + nb * 16 + cq;
-      const uint32_t off =
-          (r < mv && col < g.n_out) ? rowoff + static_cast<uint32_t>(col) * 2u : 0xFFFFFFF0u;
-      last = u32x2{swiglu_pack(acc[j][nb][0], acc[j][nb][1], acc[j][nb + 2][0], acc[j][nb + 2][1]),
-                   swiglu_pack(acc[j][nb][2], acc[j][nb][3], acc[j][nb + 2][2], acc[j][nb + 2][3])};
-      __builtin_amdgcn_raw_buffer_store_b64(last, ro, off, 0, 0);
+      w[nb][0] = swiglu_pack(acc[j][nb][0], acc[j][nb][1], acc[j][nb + 2][0], acc[j][nb + 2][1]);
+      w[nb][1] = swiglu_pack(acc[j][nb][2], acc[j][nb][3], acc[j][nb + 2][2], acc[j][nb + 2][3]);
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      swap32(w[0][h], w[1][h]);
+      swap16(w[0][h], w[1][h]);
+    }
+    const uint32_t off = (r < mv && col < g.n_out)
+                             ? static_cast<uint32_t>(mrow0 + r) * ldo2 + static_cast<uint32_t>(col) * 2u
+                             : 0xFFFFFFF0u;
+    last = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
+    __builtin_amdgcn_raw_buffer_store_b128(last, ro, off, 0, kStoreDeviceScope);
   }
-  if constexpr (2 * NJ < kPPStores) {
+  if constexpr (NJ < kPPStores<true>) {
     const uint32_t drop = opaque_u32(0xFFFFFFF0u);
 #pragma unroll
-    for (int j = 2 * NJ; j < kPPStores; ++j) __builtin_amdgcn_raw_buffer_store_b64(last, ro, drop, 0, 0);
+    for (int j = NJ; j < kPPStores<true>; ++j) __builtin_amdgcn_raw_buffer_store_b128(last, ro, drop, 0, 0);
   }
-  return kPPStores;
+  return kPPStores<true>;
 }
 
 // Down tile epilogue of one wave, staged through the wave's own 2 KiB LDS
@@ -542,7 +572,7 @@ __device__ __forceinline__ int gate_up_epilogue(const FfnGroup& g, const f32x4 (
 // runs it while group 1 issues its last MFMAs, group 1 while group 0 issues
 // the next tile's first ones.  Rows past mv and columns past n_out get an
 // offset past the buffer's bound (dropped), and a short tile pads with
-// dropped stores, so a wave issues exactly kPPStores store instructions.
+// dropped stores, so a wave issues exactly kPPStores<false> store instructions.
 template <int NJ>
 __device__ __forceinline__ int wave_staged_epilogue(const FfnGroup& g, const f32x4 (&acc)[NJ][4],
                                                     int wm, int wn, int nt, int mrow0, int mv,
@@ -577,12 +607,12 @@ __device__ __forceinline__ int wave_staged_epilogue(const FfnGroup& g, const f32
       last = v;
     }
   }
-  if constexpr (2 * NJ < kPPStores) {
+  if constexpr (2 * NJ < kPPStores<false>) {
     const uint32_t drop = opaque_u32(0xFFFFFFF0u);
 #pragma unroll
-    for (int j = 2 * NJ; j < kPPStores; ++j) __builtin_amdgcn_raw_buffer_store_b128(last, ro, drop, 0, 0);
+    for (int j = 2 * NJ; j < kPPStores<false>; ++j) __builtin_amdgcn_raw_buffer_store_b128(last, ro, drop, 0, 0);
   }
-  return kPPStores;
+  return kPPStores<false>;
 }
 
 // In the 2-stage kernel tiles run back to back: the first stage of the next
@@ -1204,7 +1234,7 @@ __device__ __forceinline__ void pp_tile(const FfnLaunch& a, const int* tstart, c
   {  // step 0: the previous tile's stores may stay in flight
     pp_issue_a<NA>(cur, 2, X1, wave);
     pp_issue_w(cur, 3, B3, wave, lane16);
-    PP_PHASES(0, X0, B0, PP_WAIT_NA(kPPStores))
+    PP_PHASES(0, X0, B0, PP_WAIT_NA(kPPStores<SWIGLU>))
   }
   int st = 0;
   PP_STEP_MID(1, X0, B1, X1, B0)
