@@ -18,7 +18,9 @@ step.  `layer` gives the whole layer's MFMA fraction and the median, min and
 max step time from the same events.  For the V3 prefill workload the line
 also carries `decode` (T = 128) and `skew` (T = 16384, capacity 640)
 objects: the same layer and weights timed in the same process.  `clocks`
-samples the graphics clock during the timed loop, `environment` names the
+is the shader clock per long launch read with GRBM_GUI_ACTIVE in the
+committed profile of the workload (null when the library's device code is
+not the profiled one), `environment` names the
 GPU, ROCm, torch and host CPU, and `wave_placement` checks the SIMD pairing
 the prefill GEMM schedule relies on.  `cpu_baseline` is the single-threaded
 C oracle on a bounded sample of tokens of the same workload.
@@ -141,10 +143,10 @@ def code_object_digest(kernel: str, lib_path: str = LIB_PATH):
     return None
 
 
-def load_traffic(workload: str):
-    """Measured HBM bytes per launch of the gate/up kernel from the committed
-    rocprofv3 counter summary, if it was taken on the device code this
-    library holds (same code object digest)."""
+def load_record(workload: str):
+    """The committed rocprofv3 record of the workload (gate/up HBM bytes per
+    launch, shader clock per launch), if it was taken on the device code
+    this library holds (same code object digest); else None."""
     path = os.path.join(ROOT, "profiles", f"ffn_gate_up_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -153,7 +155,15 @@ def load_traffic(workload: str):
     cur = code_object_digest(GATE_UP_KERNEL)
     if cur is None or rec.get("code_object_digest") != cur:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def profiled_clocks(rec):
+    """Shader clock of the workload's long launches, from its record."""
+    if not rec or not rec.get("sclk_mhz"):
+        return None
+    return {"source": f"GRBM_GUI_ACTIVE per launch, profiles/ffn_gate_up_traffic_{rec['workload']}.json",
+            "mhz": rec["sclk_mhz"]}
 
 
 def cpu_baseline(wl, inp, sample: int) -> dict:
@@ -330,7 +340,7 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
         lines.append(f"{k:60s} {fetch.get(k, 0.0):14.1f} {write.get(k, 0.0):12.1f} {fb + wb:16.4g}")
     # shader clock during each launch: GRBM_GUI_ACTIVE (GPU-busy cycles of
     # the graphics clock) over the dispatch's own duration in the same run
-    clk = {}
+    clk, clk_mhz = {}, {}
     for r in _csv_rows(os.path.join(d, "clock", "**", "*counter_collection.csv")):
         if r["Counter_Name"] != "GRBM_GUI_ACTIVE" or "moe::" not in r["Kernel_Name"]:
             continue
@@ -351,7 +361,8 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
         for k in sorted(clk, key=lambda n: -sum(ns for _, ns in clk[n])):
             cyc = sum(c for c, _ in clk[k])
             ns = sum(n for _, n in clk[k])
-            lines.append(f"{k:60s} {len(clk[k]):8d} {1e3 * cyc / ns / nxcc:8.0f}")
+            clk_mhz[k] = round(1e3 * cyc / ns / nxcc)
+            lines.append(f"{k:60s} {len(clk[k]):8d} {clk_mhz[k]:8d}")
     # vector L1 -> L2 requests of the large kernels (per-CU counters summed
     # over the CUs), with GRBM_GUI_ACTIVE of the same run for the cycles
     tcp = {}
@@ -391,61 +402,12 @@ def summarize_profile(d: str, workload: str, commands: dict, steps: int):
                "fetch_kib": fetch.get(k), "write_kib": write.get(k),
                "fetch_scale": f_scale, "write_scale": w_scale,
                "avg_launch_us": avg.get(k), "code_object_digest": code_object_digest(GATE_UP_KERNEL),
+               "sclk_mhz": {n: v for n, v in clk_mhz.items()
+                            if avg.get(n, 0.0) >= 100.0},  # launches of 0.1 ms and longer
                "commands": commands}
         with open(os.path.join(ROOT, "profiles", f"ffn_gate_up_traffic_{workload}.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
     print("\n".join(lines))
-
-
-class ClockSampler:
-    """Samples the GPU's current graphics clock (amdsmi) from a host thread
-    while a timed loop runs; nothing is sent to the GPU's queues."""
-
-    def __init__(self, period_s: float = 0.005):
-        self.period = period_s
-        self.samples = []
-        self.handle = None
-        self.thread = None
-        self.stop = False
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            dev = int(os.environ.get("HIP_VISIBLE_DEVICES", "0").split(",")[0] or 0)
-            self.handle = handles[0 if len(handles) == 1 else dev]
-            self.amdsmi = amdsmi
-        except Exception:  # no SMI access: clocks are reported as null
-            self.handle = None
-
-    def _run(self):
-        while not self.stop:
-            try:
-                info = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.GFX)
-                self.samples.append(float(info["clk"]))
-            except Exception:
-                return
-            time.sleep(self.period)
-
-    def __enter__(self):
-        import threading
-        self.samples = []
-        self.stop = False
-        if self.handle is not None:
-            self.thread = threading.Thread(target=self._run, daemon=True)
-            self.thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self.stop = True
-        if self.thread is not None:
-            self.thread.join()
-
-    def summary(self):
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"sclk_mhz_mean": round(sum(v) / len(v), 1), "sclk_mhz_min": v[0],
-                "sclk_mhz_max": v[-1], "samples": len(v)}
 
 
 def environment(torch) -> dict:
@@ -489,7 +451,7 @@ def wave_placement(moe, torch) -> dict:
     return {"workgroups": n, "w_and_w_plus_4_share_simd": ok, "example": s[0]}
 
 
-def time_layer(moe, torch, wl, inp, weights, steps: int, warmup: int, sampler=None) -> dict:
+def time_layer(moe, torch, wl, inp, weights, steps: int, warmup: int) -> dict:
     """Warm up, then run `steps` calls of moe_layer_forward bracketed by
     synchronisations; per-stage and per-step times from HIP events recorded
     by the library on the launch stream."""
@@ -511,15 +473,11 @@ def time_layer(moe, torch, wl, inp, weights, steps: int, warmup: int, sampler=No
     ns = moe.N_STAGES + 1
     evs = hev.create(steps * ns)
     torch.cuda.synchronize()
-    if sampler is not None:
-        sampler.__enter__()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i * ns:(i + 1) * ns])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    if sampler is not None:
-        sampler.__exit__(None, None, None)
     stage_ms = [0.0] * moe.N_STAGES
     step_ms = []
     for i in range(steps):
@@ -605,10 +563,8 @@ def main():
                                   {n: inp[n] for n in ("w_router", "w13", "w2", "ws13", "ws2")})
     torch.cuda.synchronize()
 
-    sampler = ClockSampler()
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    m = time_layer(moe, torch, wl, inp, weights, args.steps, args.warmup, sampler)
-    clocks = sampler.summary()
+    m = time_layer(moe, torch, wl, inp, weights, args.steps, args.warmup)
     ms_per_step = m["ms_per_step"]
     print(f"[bench] {ms_per_step:.3f} ms per step", file=sys.stderr, flush=True)
     kept, touched, st = m["kept"], m["touched"], m["stage_ms"]
@@ -617,7 +573,8 @@ def main():
 
     gate_up_ms = st["ffn_gate_up"]
     achieved_tflops = work["gate_up_flop"] / (gate_up_ms / 1e3) / 1e12
-    traffic = load_traffic(args.workload)
+    rec = load_record(args.workload)
+    traffic = rec.get("bytes_per_launch") if rec else None
     # algorithmic bytes of the gate/up launch: the touched experts' gate/up
     # weights, the shared expert's, x once, h written once
     es = 2 if wl.act_dtype == 1 else 4
@@ -669,21 +626,21 @@ def main():
                   "step_ms": m["step_ms"], "kept_rows": kept, "touched_experts": touched,
                   "hbm_frac_touched_weights": round(tb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "stage_ms": {k: round(v, 4) for k, v in st.items()}},
-        "clocks": clocks,
+        "clocks": profiled_clocks(rec),
     }
     if wl.name == workloads.V3_PREFILL.name and not args.no_extra:
         # the decode and skew configurations of the same layer, same weights,
         # same process
         extra = {}
-        for name, sub in (("decode", workloads.V3_DECODE), ("skew", workloads.V3_SKEW)):
+        for name, key, sub in (("decode", "v3_decode", workloads.V3_DECODE),
+                               ("skew", "v3_skew", workloads.V3_SKEW)):
             si = dict(inp)
             si["x"] = synth.normal((sub.T, sub.H), sub.x_std, torch.bfloat16, dev, sub.seed,
                                    f"x_T{sub.T}")
             if sub.bias_kind == "zipf":
                 si["bias"] = synth.zipf_bias(sub.N, sub.bias_param, dev, sub.seed)
             print(f"[bench] {name}: {sub.name}", file=sys.stderr, flush=True)
-            smp = ClockSampler()
-            r = time_layer(moe, torch, sub, si, weights, args.steps, args.warmup, smp)
+            r = time_layer(moe, torch, sub, si, weights, args.steps, args.warmup)
             tbs = touched_weight_bytes(sub, r["touched"])
             wk = algorithmic_work(sub, r["kept"])
             e = {"workload": sub.name, "ms_per_step": round(r["ms_per_step"], 4),
@@ -695,7 +652,7 @@ def main():
                  "mfma_frac": round(wk["layer_flop"] / (r["step_ms"]["median"] / 1e3) / 1e12
                                     / MFMA_BF16_PEAK_TFLOPS, 4),
                  "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
-                 "clocks": smp.summary()}
+                 "clocks": profiled_clocks(load_record(key))}
             if sub.capacity:
                 e["dropped_assignments"], e["tokens_all_dropped"] = r["n_dropped"]
                 e["capacity"] = sub.capacity
