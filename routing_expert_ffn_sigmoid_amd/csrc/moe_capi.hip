@@ -121,10 +121,11 @@ T* at(void* ws, size_t off) {
 }
 
 // Byte bound of an operand for buffer addressing, or 0 when it does not fit
-// a 32-bit byte offset.
+// a 32-bit byte offset.  At most 0xFFFFFF00: the kernels drop a store or
+// load by giving it the offset 0xFFFFFFF0, which then lies past every bound.
 uint32_t bound32(long long rows, long long cols, size_t es) {
   const unsigned long long b = static_cast<unsigned long long>(rows) * cols * es;
-  return b < 0xFFFFFFFFull ? static_cast<uint32_t>(b) : 0u;
+  return b <= 0xFFFFFF00ull ? static_cast<uint32_t>(b) : 0u;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
