@@ -511,7 +511,8 @@ __device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
 
 // Cache-policy bits of the ping-pong epilogues' h and y stores: device
 // scope (sc1).  Measured against the default on V3 prefill, alternating in
-// one process: the gate/up launch 1-1.5 % faster, the down launch 0.1-0.8 %.
+// one process: the gate/up launch 1-1.5 % faster, the down launch 0.1-0.8 %
+// faster in four of five runs (0.3 % slower in one).
 constexpr int kStoreDeviceScope = 16;
 
 // Gate/up tile epilogue straight from registers.  Per M-block a lane holds,
