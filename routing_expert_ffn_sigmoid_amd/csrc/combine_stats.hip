@@ -144,6 +144,7 @@ hipError_t launch_combine(const void* y_perm, const int32_t* inv_row, const floa
 
 // ---------------------------------------------------------------- stats
 constexpr int kStatsMaxBlocks = 256;
+constexpr int kStatsLoads = 32;  // loads one thread keeps in flight in the statistics kernels
 
 int stats_blocks(int T) {
   int b = (T + 63) / 64;
@@ -170,15 +171,16 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
     return score_fn == MOE_SCORE_SIGMOID ? sigmoid_score(l) : __expf(l - lse[t]);
   };
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    // tokens in ascending order; eight logit loads in flight at a time
+    // tokens in ascending order; kStatsLoads logit loads in flight at a time
+    // (the launch is short and latency-bound: few rounds of memory latency)
     double acc = 0.0;
     int t = t0;
-    for (; t + 8 <= t1; t += 8) {
-      float l[8];
+    for (; t + kStatsLoads <= t1; t += kStatsLoads) {
+      float l[kStatsLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) l[u] = logits[static_cast<int64_t>(t + u) * N + e];
+      for (int u = 0; u < kStatsLoads; ++u) l[u] = logits[static_cast<int64_t>(t + u) * N + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += static_cast<double>(score(l[u], t + u));
+      for (int u = 0; u < kStatsLoads; ++u) acc += static_cast<double>(score(l[u], t + u));
     }
     for (; t < t1; ++t) acc += static_cast<double>(score(logits[static_cast<int64_t>(t) * N + e], t));
     out[e] = acc;
@@ -219,16 +221,16 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const double* __restri
                                                           float* __restrict__ scalars) {
   __shared__ double sh[4];
   const int e = threadIdx.x;
-  // column sums in block order, eight partial loads in flight at a time
+  // column sums in block order, kStatsLoads partial loads in flight at a time
   double col = 0.0;
   if (e < N) {
     int b = 0;
-    for (; b + 8 <= nblk; b += 8) {
-      double v[8];
+    for (; b + kStatsLoads <= nblk; b += kStatsLoads) {
+      double v[kStatsLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[static_cast<int64_t>(b + u) * (N + 2) + e];
+      for (int u = 0; u < kStatsLoads; ++u) v[u] = part[static_cast<int64_t>(b + u) * (N + 2) + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) col += v[u];
+      for (int u = 0; u < kStatsLoads; ++u) col += v[u];
     }
     for (; b < nblk; ++b) col += part[static_cast<int64_t>(b) * (N + 2) + e];
   }
